@@ -1,0 +1,296 @@
+/*
+ * CPU oracle for the routed weight-only-quantized (WNA16) MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code with the HIP library.
+ *
+ * Plain, slow and meant to be read against the pages.  Every value is carried
+ * in IEEE double; every sum runs in ascending index order.
+ *
+ * What it computes (the pages give the pieces, not a formula):
+ *   - Expert weights are symmetric signed b-bit codes (b = 2 or 4) packed into
+ *     32-bit words, with one FP16 scale per K group and no zero point
+ *     (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What changed" and
+ *     "How it was created" step 4).  W[n][k] = q[n][k] * s[n][k / group].
+ *   - Each routed expert is a gated MLP: a fused gate/up projection (w13) and
+ *     a down projection (w2), each with its own bit width and group size
+ *     (PR "Incubate DeepSeek V4 WNA16 runtime on SM86", "What this branch
+ *     adds" item 2, "Validation completed" on projection-specific groups).
+ *   - Activations are BF16 and every token carries top-k expert indices
+ *     (same PR, item 3, "BF16 indexed MoE").
+ *   - The gate/up pair goes through SwiGLU with alpha, beta and clamp
+ *     (same PR, item 9).
+ *   - out[t] = sum_j w[t][j] * W2_e * SwiGLU(W13_e x_t), e = ids[t][j].
+ *
+ * Readings where the pages are silent (each one is also listed in the design
+ * notes of this repository):
+ *   R1 words are row-major [rows][K*b/32]: row n holds the K-contiguous codes
+ *      of output channel n.
+ *   R2 least-significant field first: K index j*(32/b)+i sits in bits
+ *      [i*b, (i+1)*b) of word j.
+ *   R3 offset binary: stored field u = q + 2^(b-1).
+ *   R5 scales are [rows][K/group]; a group runs along K only.
+ *   R6 g' = min(g, c), u' = clamp(u, -c, c), act = g' * sigmoid(alpha g') * (u' + beta);
+ *      c = +inf means no clamp.
+ *   R7 w13 rows [0, I) are the gate (w1), rows [I, 2I) the up projection (w3).
+ *   R8 the routing weight multiplies the expert output; weights are used as
+ *      given (no renormalisation).  Ids outside [0, E) contribute nothing.
+ *   R12 alignment contract of the expert-sorted tiles (see oracle_align).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16 -> double.  Field layout: 1 sign, 5 exponent (bias 15),
+ * 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);              /* subnormal: m * 2^(1-15-10) */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);  /* (1 + m/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double.  Field layout: 1 sign, 8 exponent (bias 127),
+ * 7 fraction bits. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int m = b & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);             /* subnormal: m * 2^(1-127-7) */
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134);  /* (1 + m/2^7) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+/* Signed code at K index k of one packed row (readings R2, R3). */
+int oracle_code(const uint32_t *row_words, int k, int bits)
+{
+    int per_word = 32 / bits;
+    uint32_t word = row_words[k / per_word];
+    int field = k % per_word;
+    uint32_t u = (word >> (field * bits)) & ((1u << bits) - 1u);
+    return (int)u - (1 << (bits - 1));
+}
+
+/* Dequantized weight W[n][k] = q * s (reading R5). */
+double oracle_weight(const uint32_t *words, const uint16_t *scales, int K, int bits,
+                     int group, int n, int k)
+{
+    const uint32_t *row = words + (size_t)n * (size_t)(K * bits / 32);
+    double s = oracle_f16_to_f64(scales[(size_t)n * (size_t)(K / group) + (size_t)(k / group)]);
+    return (double)oracle_code(row, k, bits) * s;
+}
+
+/* y[n] = sum_k W[n][k] * v[k] for n in [0, rows), ascending k. */
+void oracle_qmatvec(const uint32_t *words, const uint16_t *scales, int rows, int K, int bits,
+                    int group, const double *v, double *y)
+{
+    for (int n = 0; n < rows; ++n) {
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k)
+            acc += oracle_weight(words, scales, K, bits, group, n, k) * v[k];
+        y[n] = acc;
+    }
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* SwiGLU with alpha, beta and clamp (reading R6). */
+double oracle_swiglu(double g, double u, double alpha, double beta, double clamp)
+{
+    double gc = g < clamp ? g : clamp;
+    double uc = u < -clamp ? -clamp : (u > clamp ? clamp : u);
+    return gc * sigmoid(alpha * gc) * (uc + beta);
+}
+
+/* One expert on one token: y = W2_e * SwiGLU(W13_e x).  x has H entries, y has
+ * H entries.  Work space: h (2I) and act (I). */
+void oracle_expert(const uint32_t *w13, const uint16_t *s13, const uint32_t *w2,
+                   const uint16_t *s2, int H, int I, int bits13, int group13, int bits2,
+                   int group2, double alpha, double beta, double clamp, const double *x,
+                   double *h, double *act, double *y)
+{
+    oracle_qmatvec(w13, s13, 2 * I, H, bits13, group13, x, h);
+    for (int i = 0; i < I; ++i)
+        act[i] = oracle_swiglu(h[i], h[I + i], alpha, beta, clamp);
+    oracle_qmatvec(w2, s2, H, I, bits2, group2, act, y);
+}
+
+/*
+ * Routed layer for the tokens listed in `tokens` (ntok of them); row r of
+ * `out` ([ntok][H]) is the result for token tokens[r].  Passing every token in
+ * order gives the whole layer.  Per-(token, slot) expert outputs are computed
+ * independently (in parallel when OpenMP is on, `nthreads` <= 0 meaning its
+ * default) and then summed per token in slot order j = 0..k-1.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_moe_forward_tokens(const uint16_t *x, const int32_t *ids, const float *topk_w,
+                              const uint32_t *w13, const uint16_t *s13, const uint32_t *w2,
+                              const uint16_t *s2, int T, int H, int I, int E, int topk,
+                              int bits13, int group13, int bits2, int group2, double alpha,
+                              double beta, double clamp, const int32_t *tokens, int ntok,
+                              double *out, int nthreads)
+{
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || ntok < 0)
+        return -1;
+    if ((bits13 != 2 && bits13 != 4) || (bits2 != 2 && bits2 != 4))
+        return -1;
+    if (group13 <= 0 || group2 <= 0 || H % group13 || I % group2)
+        return -1;
+    if ((H * bits13) % 32 || (I * bits2) % 32)
+        return -1;
+    for (int r = 0; r < ntok; ++r)
+        if (tokens[r] < 0 || tokens[r] >= T)
+            return -1;
+
+    const size_t w13_expert = (size_t)2 * I * (size_t)(H * bits13 / 32);
+    const size_t s13_expert = (size_t)2 * I * (size_t)(H / group13);
+    const size_t w2_expert = (size_t)H * (size_t)(I * bits2 / 32);
+    const size_t s2_expert = (size_t)H * (size_t)(I / group2);
+    const long npairs = (long)ntok * topk;
+
+    double *ybuf = (double *)calloc((size_t)(npairs > 0 ? npairs : 1) * (size_t)H, sizeof(double));
+    int *used = (int *)calloc((size_t)(npairs > 0 ? npairs : 1), sizeof(int));
+    if (!ybuf || !used) {
+        free(ybuf);
+        free(used);
+        return -1;
+    }
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+    {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+        double *h = (double *)malloc(sizeof(double) * (size_t)2 * I);
+        double *act = (double *)malloc(sizeof(double) * (size_t)I);
+        if (!xv || !h || !act) {
+            bad = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+            for (long pr = 0; pr < npairs; ++pr) {
+                int t = tokens[pr / topk];
+                int j = (int)(pr % topk);
+                int e = ids[(size_t)t * topk + j];
+                if (e < 0 || e >= E)
+                    continue;                    /* R8: contributes nothing */
+                for (int k = 0; k < H; ++k)
+                    xv[k] = oracle_bf16_to_f64(x[(size_t)t * H + k]);
+                oracle_expert(w13 + (size_t)e * w13_expert, s13 + (size_t)e * s13_expert,
+                              w2 + (size_t)e * w2_expert, s2 + (size_t)e * s2_expert, H, I,
+                              bits13, group13, bits2, group2, alpha, beta, clamp, xv, h, act,
+                              ybuf + (size_t)pr * H);
+                used[pr] = 1;
+            }
+        }
+        free(xv);
+        free(h);
+        free(act);
+    }
+    if (!bad) {
+        for (int r = 0; r < ntok; ++r) {
+            double *o = out + (size_t)r * H;
+            for (int n = 0; n < H; ++n)
+                o[n] = 0.0;
+            int t = tokens[r];
+            for (int j = 0; j < topk; ++j) {
+                long pr = (long)r * topk + j;
+                if (!used[pr])
+                    continue;
+                double w = (double)topk_w[(size_t)t * topk + j];
+                const double *y = ybuf + (size_t)pr * H;
+                for (int n = 0; n < H; ++n)
+                    o[n] += w * y[n];
+            }
+        }
+    }
+    free(ybuf);
+    free(used);
+    return bad ? -1 : 0;
+}
+
+/*
+ * Expert-sorted tile layout of the (token, slot) pairs (reading R12).
+ *
+ * Pair p = t*topk + j has expert ids[p].  counts[e] = number of pairs with
+ * expert e.  expert_offsets (E+1 entries) is the exclusive prefix sum of
+ * counts rounded up to a multiple of block_m; its last entry is the padded
+ * total.  sorted_ids[expert_offsets[e] + r] is the r-th smallest pair index
+ * with expert e (a stable counting sort); the padding slots of each expert
+ * hold P = T*topk.  tile_expert[b] = e for every tile b of block_m slots in
+ * e's range; num_tiles = padded total / block_m.  inv_perm[p] is the slot of
+ * pair p, or -1 when ids[p] lies outside [0, E) (such pairs are skipped and
+ * counted in *bad_ids).  Buffers must hold the padded total (sorted_ids), the
+ * tile count (tile_expert) and P (inv_perm) entries.  Returns 0 or -1.
+ */
+int oracle_align(const int32_t *ids, int T, int topk, int E, int block_m, int32_t *sorted_ids,
+                 int32_t *tile_expert, int32_t *expert_offsets, int32_t *inv_perm,
+                 int32_t *num_tiles, int32_t *bad_ids)
+{
+    if (T < 0 || topk <= 0 || E <= 0 || block_m <= 0)
+        return -1;
+    const long P = (long)T * topk;
+    long *counts = (long *)calloc((size_t)E, sizeof(long));
+    long *fill = (long *)calloc((size_t)E, sizeof(long));
+    if (!counts || !fill) {
+        free(counts);
+        free(fill);
+        return -1;
+    }
+    long bad = 0;
+    for (long p = 0; p < P; ++p) {
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            ++bad;
+        else
+            ++counts[e];
+    }
+    long off = 0;
+    for (int e = 0; e < E; ++e) {
+        expert_offsets[e] = (int32_t)off;
+        long padded = (counts[e] + block_m - 1) / block_m * block_m;
+        for (long s = off; s < off + padded; ++s)
+            sorted_ids[s] = (int32_t)P;
+        for (long b = off / block_m; b < (off + padded) / block_m; ++b)
+            tile_expert[b] = e;
+        off += padded;
+    }
+    expert_offsets[E] = (int32_t)off;
+    for (long p = 0; p < P; ++p) {
+        int e = ids[p];
+        if (e < 0 || e >= E) {
+            inv_perm[p] = -1;
+            continue;
+        }
+        long slot = expert_offsets[e] + fill[e]++;
+        sorted_ids[slot] = (int32_t)p;
+        inv_perm[p] = (int32_t)slot;
+    }
+    *num_tiles = (int32_t)(off / block_m);
+    *bad_ids = (int32_t)bad;
+    free(counts);
+    free(fill);
+    return 0;
+}

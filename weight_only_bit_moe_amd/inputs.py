@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for the routed WNA16 MoE layer.
+
+This module only draws inputs.  It holds none of the layer's arithmetic: no
+unpacking, no dequantization, no activation, no routing sums.  Both the CPU
+oracle (through the tests) and the HIP library consume exactly the arrays built
+here, so the two sides see identical bytes.
+
+Workloads follow the pages' formats: symmetric 2-bit / 4-bit signed codes packed
+into 32-bit words with one FP16 scale per K group (model card
+"hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What changed"), fused gate/up (w13)
+and down (w2) projections with their own bit width and group size (PR "Incubate
+DeepSeek V4 WNA16 runtime on SM86", "What this branch adds" items 2 and 9, and
+"Validation completed"), BF16 activations and top-k indexed routing (same PR,
+item 3).
+
+Codes are drawn as uniform random 32-bit words.  Every code field of a word is
+then uniform over the full b-bit range, which is exactly the code
+distribution the workloads ask for ([-2, 1] for 2-bit, [-8, 7] for 4-bit), and
+it is so under any sign encoding of the field.
+
+Draw order for one layer (fixed, so a seed names the bytes):
+  1. routing ids   2. routing weights   3. x   4. outlier channels
+  5. w13 words     6. w13 scales        7. w2 words   8. w2 scales
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Layer",
+    "LayerSpec",
+    "CONFIGS",
+    "make_layer",
+    "make_config",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    """Shape, format and distribution recipe of one synthetic layer."""
+
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    topk: int
+    bits13: int
+    group13: int
+    bits2: int
+    group2: int
+    routing: str = "uniform"          # "uniform" | "zipf"
+    zipf_s: float = 1.1
+    scale_lo: float = 0.01
+    scale_hi: float = 0.05
+    scale_dist: str = "uniform"       # "uniform" | "loguniform"
+    x_sigma: float = 1.0
+    outlier_frac: float = 0.0         # fraction of hidden channels scaled up
+    outlier_mult: float = 10.0
+    alpha: float = 1.0
+    beta: float = 0.0
+    clamp: float = math.inf
+
+    def replace(self, **kw) -> "LayerSpec":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass
+class Layer:
+    """Host arrays of one layer, in the boundary's layouts.
+
+    x           uint16 [T, H]            bf16 bit patterns, row-major
+    topk_ids    int32  [T, k]
+    topk_w      float32[T, k]
+    w13         uint32 [E, 2I, H*b13/32] rows 0..I-1 gate (w1), I..2I-1 up (w3)
+    s13         float16[E, 2I, H/g13]
+    w2          uint32 [E, H, I*b2/32]
+    s2          float16[E, H, I/g2]
+    """
+
+    spec: LayerSpec
+    x: np.ndarray
+    topk_ids: np.ndarray
+    topk_w: np.ndarray
+    w13: np.ndarray
+    s13: np.ndarray
+    w2: np.ndarray
+    s2: np.ndarray
+    outlier_channels: np.ndarray
+
+    @property
+    def T(self):
+        return self.spec.T
+
+    @property
+    def H(self):
+        return self.spec.H
+
+    @property
+    def I(self):
+        return self.spec.I
+
+    @property
+    def E(self):
+        return self.spec.E
+
+    @property
+    def topk(self):
+        return self.spec.topk
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns.  Inputs are finite by construction here.
+    """
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    r = (b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _routing_ids(rng: np.random.Generator, spec: LayerSpec) -> np.ndarray:
+    T, E, k = spec.T, spec.E, spec.topk
+    if k > E:
+        raise ValueError("distinct top-k routing needs topk <= E")
+    if spec.routing == "uniform":
+        # first k entries of an independent uniform permutation of the experts
+        perms = rng.permuted(np.tile(np.arange(E, dtype=np.int64), (max(T, 1), 1)), axis=1)[:T]
+        return perms[:, :k].astype(np.int32)
+    if spec.routing == "zipf":
+        # expert of popularity rank r (1-based) has probability proportional to
+        # r**-s; ranks are assigned through a seeded permutation of the experts.
+        perm = rng.permutation(E)
+        logp = np.empty(E, dtype=np.float64)
+        logp[perm] = -spec.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))
+        # k distinct draws without replacement: Gumbel top-k on log p
+        keys = logp[None, :] + rng.gumbel(size=(T, E))
+        order = np.argsort(-keys, axis=1, kind="stable")
+        return order[:, :k].astype(np.int32)
+    raise ValueError(f"unknown routing {spec.routing!r}")
+
+
+def _scales(rng: np.random.Generator, spec: LayerSpec, shape) -> np.ndarray:
+    if spec.scale_dist == "uniform":
+        s = rng.uniform(spec.scale_lo, spec.scale_hi, size=shape)
+    elif spec.scale_dist == "loguniform":
+        s = np.exp(rng.uniform(math.log(spec.scale_lo), math.log(spec.scale_hi), size=shape))
+    else:
+        raise ValueError(spec.scale_dist)
+    return s.astype(np.float16)  # float64 -> float16, round to nearest even
+
+
+def make_layer(spec: LayerSpec, seed: int, topk_ids: Optional[np.ndarray] = None) -> Layer:
+    """Draw one layer.  `topk_ids`, when given, replaces the routing draw
+    (the routing-id draws are still made so the other arrays keep their bytes)."""
+    T, H, I, E, k = spec.T, spec.H, spec.I, spec.E, spec.topk
+    rng = np.random.default_rng(seed)
+    ids = _routing_ids(rng, spec) if T > 0 else np.zeros((0, k), np.int32)
+    if topk_ids is not None:
+        ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(T, k)
+    logits = rng.standard_normal((T, k))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True)) if T > 0 else logits
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32) if T > 0 else w.astype(np.float32)
+    xf = (rng.standard_normal((T, H)) * spec.x_sigma).astype(np.float32)
+    n_out = int(round(spec.outlier_frac * H))
+    out_ch = np.sort(rng.choice(H, size=n_out, replace=False)) if n_out > 0 else np.zeros(0, np.int64)
+    if n_out:
+        xf[:, out_ch] *= np.float32(spec.outlier_mult)
+    x = f32_to_bf16_bits(xf)
+    w13 = rng.integers(0, 2**32, size=(E, 2 * I, H * spec.bits13 // 32), dtype=np.uint32)
+    s13 = _scales(rng, spec, (E, 2 * I, H // spec.group13))
+    w2 = rng.integers(0, 2**32, size=(E, H, I * spec.bits2 // 32), dtype=np.uint32)
+    s2 = _scales(rng, spec, (E, H, I // spec.group2))
+    return Layer(spec, x, ids, w, w13, s13, w2, s2, out_ch.astype(np.int64))
+
+
+_BIG = dict(H=4096, I=2048, E=256)
+
+#: The five named workloads.  Values follow the configuration list this project
+#: measures on; where a workload leaves a distribution unstated it reuses the
+#: closest stated one (prefill-chunk codes and scales as in the decode W2 layer).
+CONFIGS = {
+    1: LayerSpec("tiny-w4g128-T8", T=8, H=256, I=128, E=8, topk=2, bits13=4, group13=128,
+                 bits2=4, group2=128, routing="uniform", scale_lo=0.005, scale_hi=0.02),
+    2: LayerSpec("decode-w2g128-T4", T=4, **_BIG, topk=6, bits13=2, group13=128, bits2=2,
+                 group2=128, routing="uniform", scale_lo=0.01, scale_hi=0.05),
+    3: LayerSpec("batched-decode-w4g128-T64", T=64, **_BIG, topk=6, bits13=4, group13=128,
+                 bits2=4, group2=128, routing="uniform", scale_lo=0.002, scale_hi=0.01),
+    4: LayerSpec("prefill-w2g128-T2048-zipf", T=2048, **_BIG, topk=6, bits13=2, group13=128,
+                 bits2=2, group2=128, routing="zipf", scale_lo=0.01, scale_hi=0.05,
+                 alpha=1.702, beta=1.0, clamp=7.0),
+    5: LayerSpec("prefill-w4g128-w2g64-T8192-zipf", T=8192, **_BIG, topk=8, bits13=4,
+                 group13=128, bits2=2, group2=64, routing="zipf", scale_lo=1e-3, scale_hi=5e-2,
+                 scale_dist="loguniform", x_sigma=2.0, outlier_frac=0.01, alpha=1.702,
+                 beta=1.0, clamp=7.0),
+}
+
+
+def make_config(idx: int, seed: Optional[int] = None) -> Layer:
+    """Layer of named workload `idx` (1..5); the seed defaults to `idx`."""
+    return make_layer(CONFIGS[idx], idx if seed is None else seed)
