@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed WNA16 MoE layer on one MI355X.
+
+One step = one full layer (route + w13/SwiGLU + w2/scatter-add + convert) over
+one batch of synthetic tokens, with every input already resident in HBM.
+Each step uses a different routing batch drawn from the workload's
+distributions (the expert weights stay the same), so consecutive steps touch
+mostly different experts and the weight stream comes from HBM rather than
+from the 256 MB last-level cache.
+
+The default workload is the decode-sized W2A16 layer (T=4, hidden 4096,
+intermediate 2048, 256 experts, top-6, 2-bit codes, group 128), which is
+HBM-bound; `--config 3/4/5` selects the other workloads.
+
+Prints ONE JSON line.  `roofline` is for the kernel with the longest average
+duration, timed live by the kernel dispatches' own start/stop events
+(moe_wna16_forward_profiled) over the timed region.  `cpu_baseline` is the CPU
+oracle on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import ctypes.util
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
+KERNELS = ("route", "w13", "w2", "convert")
+KERNEL_SOURCE = os.path.join(ROOT, "weight_only_bit_moe_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--batches", type=int, default=64,
+                    help="distinct routing batches cycled over the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--traffic-file", default=None,
+                    help="rocprofv3 counter summary holding the dominant kernel's HBM traffic")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs (events)."""
+
+    def __init__(self):
+        path = ctypes.util.find_library("amdhip64") or "/opt/rocm/lib/libamdhip64.so"
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def per_expert_bytes(bits, group, rows, K):
+    """Packed codes + FP16 scales of one expert's projection."""
+    return rows * K * bits // 8 + rows * (K // group) * 2
+
+
+def kernel_traffic(path, kernel):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    if not path or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    want = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(rf"traffic_bytes_per_launch\[{kernel}\]:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != want:
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this layer has no multi-GPU path here "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import weight_only_bit_moe_amd as M
+    from weight_only_bit_moe_amd.inputs import CONFIGS, make_batch, make_config
+
+    if not os.path.exists(M.LIB_PATH):
+        from weight_only_bit_moe_amd import build as hip_build
+        hip_build.build()
+
+    cfg = args.config
+    decode = cfg in (2, 3)
+    steps = args.steps if args.steps is not None else (200 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    L = make_config(cfg)
+    sp = L.spec
+    T, H, I, E, k = sp.T, sp.H, sp.I, sp.E, sp.topk
+    P = T * k
+    w13 = torch.from_numpy(L.w13.view(np.int32)).to(dev)
+    s13 = torch.from_numpy(L.s13).to(dev)
+    w2 = torch.from_numpy(L.w2.view(np.int32)).to(dev)
+    s2 = torch.from_numpy(L.s2).to(dev)
+    nb = max(1, min(args.batches, steps))
+    host_batches = [(L.topk_ids, L.topk_w, L.x)]
+    for i in range(1, nb):
+        host_batches.append(make_batch(sp, seed=cfg * 100000 + i,
+                                       outlier_channels=L.outlier_channels))
+    batches = []
+    for ids, w, x in host_batches:
+        batches.append((torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16),
+                        torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)))
+    ws = M.workspace_for(T, H, I, E, k, dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    q13, q2 = (sp.bits13, sp.group13), (sp.bits2, sp.group2)
+    clamp = sp.clamp
+    fixed = (w13.data_ptr(), s13.data_ptr(), w2.data_ptr(), s2.data_ptr())
+    call_args = []
+    for x, ids, w in batches:
+        call_args.append((x.data_ptr(), ids.data_ptr(), w.data_ptr()) + fixed +
+                         (T, H, I, E, k, q13, q2, sp.alpha, sp.beta, clamp, out.data_ptr(),
+                          ws.data_ptr(), ws.numel(), stream))
+    plan = M.moe_wna16_plan(T, H, I, E, k, q13, q2)
+
+    def step_plain(i):
+        st = M.moe_wna16_forward(*call_args[i % nb])
+        if st != 0:
+            raise M.MoeWna16Error(st, "moe_wna16_forward")
+
+    hip = Hip()
+    events = [(ctypes.c_void_p * 8)(*[hip.event() for _ in range(8)]) for _ in range(steps)]
+
+    for i in range(warmup):
+        step_plain(i)
+    torch.cuda.synchronize(dev)
+
+    # timed region: K profiled steps (dispatch-packet events, no extra packets)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st = M.moe_wna16_forward_profiled(*call_args[i % nb], events[i])
+        if st != 0:
+            raise M.MoeWna16Error(st, "moe_wna16_forward_profiled")
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    kern_ms = {name: [] for name in KERNELS}
+    step_gpu_ms = []
+    for i in range(steps):
+        ev = events[i]
+        for j, name in enumerate(KERNELS):
+            kern_ms[name].append(hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]))
+        step_gpu_ms.append(hip.elapsed_ms(ev[0], ev[7]))
+    avg = {n: float(np.mean(v)) for n, v in kern_ms.items()}
+
+    # same steps through the plain entry point, for reference
+    torch.cuda.synchronize(dev)
+    t2 = time.perf_counter()
+    for i in range(steps):
+        step_plain(i)
+    torch.cuda.synchronize(dev)
+    t3 = time.perf_counter()
+    ms_plain = (t3 - t2) * 1e3 / steps
+
+    # algorithmic work of each step (bookkeeping from the routing ids)
+    b13 = per_expert_bytes(sp.bits13, sp.group13, 2 * I, H)
+    b2 = per_expert_bytes(sp.bits2, sp.group2, H, I)
+    touched = []
+    for i in range(steps):
+        ids = host_batches[i % nb][0]
+        touched.append(len(np.unique(ids[(ids >= 0) & (ids < E)])))
+    mean_touched = float(np.mean(touched))
+    alg_bytes = {
+        "w13": mean_touched * b13 + T * H * 2 + P * I * 2,
+        "w2": mean_touched * b2 + P * I * 2 + T * H * 4,
+    }
+    alg_flops = {"w13": 2.0 * P * 2 * I * H, "w2": 2.0 * P * H * I}
+    layer_bytes = mean_touched * (b13 + b2) + T * H * 2 * 2
+    layer_flops = alg_flops["w13"] + alg_flops["w2"]
+
+    dom = max(("w13", "w2"), key=lambda n: avg[n])
+    if decode:
+        achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = alg_flops[dom] / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS}
+    roof["kernel"] = dom
+    roof["kernel_ms"] = avg[dom]
+    roof["algorithmic_bytes" if decode else "algorithmic_flops"] = (
+        alg_bytes[dom] if decode else alg_flops[dom])
+    traffic_file = args.traffic_file or os.path.join(
+        ROOT, "profiles", f"{dom}_{sp.name}_counters.md")
+    roof["traffic"] = kernel_traffic(traffic_file, dom)
+
+    value = T / (ms_per_step * 1e-3)
+    result = {
+        "metric": "routed-MoE layer tokens/s on 1 MI355X",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; fresh routing batch per step)",
+        "config": {"workload": sp.name, "T": T, "hidden": H, "intermediate": I, "experts": E,
+                   "topk": k, "w13": f"W{sp.bits13} g{sp.group13}",
+                   "w2": f"W{sp.bits2} g{sp.group2}", "block_m": plan["block_m"],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "kernel_ms": avg,
+        "gpu_ms_per_step_events": float(np.mean(step_gpu_ms)),
+        "ms_per_step_unprofiled": ms_plain,
+        "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_mfma_frac": layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "experts_touched_per_step": mean_touched,
+    }
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    for e in events:
+        for h in e:
+            hip.destroy(h)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(L, budget_s):
+    """The CPU oracle (float64, OpenMP over (token, slot) pairs) timed on this
+    host over a bounded sample of the workload's tokens."""
+    import numpy as np
+
+    from oracle import oracle
+
+    sp = L.spec
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    # sample: whole batches when the batch is small, else a slice of tokens
+    t0 = time.perf_counter()
+    probe = oracle.forward_layer(L, tokens=[0], nthreads=threads)
+    per_token = time.perf_counter() - t0
+    ntok = int(max(1, min(sp.T, budget_s / max(per_token, 1e-6) * min(threads, sp.topk))))
+    tokens = list(range(ntok))
+    done, elapsed, reps = 0, 0.0, 0
+    while elapsed < budget_s * 0.5 or reps == 0:
+        t0 = time.perf_counter()
+        oracle.forward_layer(L, tokens=tokens, nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        done += ntok
+        reps += 1
+        if ntok < sp.T:
+            break
+    used = min(threads, ntok * sp.topk)
+    del probe
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{ntok} of {sp.T} tokens x {reps} pass(es) of workload {sp.name}, "
+                      f"{elapsed:.1f} s, float64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * moe_wna16.h -- C ABI of the routed weight-only-quantized (WNA16) MoE layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (PR "Incubate DeepSeek V4 WNA16 runtime on SM86", "What this
+ * branch adds" items 1-3 and 9; model card
+ * "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What changed"):
+ *
+ *   for every token t and each of its top-k slots j, with e = topk_ids[t][j]:
+ *     h   = W13_e x_t                    fused gate (rows 0..I-1) and up (rows I..2I-1)
+ *     a   = SwiGLU_{alpha,beta,clamp}(h[0:I], h[I:2I])
+ *     out_t += topk_w[t][j] * (W2_e a)
+ *   out is returned in BF16; the sum is carried in FP32.
+ *
+ *   W[n][k] = q[n][k] * s[n][k / group]: symmetric signed b-bit codes (b = 2 or
+ *   4, no zero point) packed into 32-bit words and one FP16 scale per group of
+ *   K elements.  Each projection has its own bit width and group size
+ *   ("Validation completed": projection-specific group sizes).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller (except
+ *     the *_out / plan arguments documented as host pointers).  The library
+ *     allocates no memory and keeps no state between calls; calls on
+ *     different streams may run concurrently.
+ *   - Work is enqueued asynchronously on `stream`; no entry point
+ *     synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     non-zero status means nothing was launched and no buffer was touched.
+ *   - Device-side values (expert ids) are not validated on the host: an id
+ *     outside [0, E) contributes nothing and is counted in the workspace.
+ *
+ * Packed formats (the pages fix the pieces; the order of fields and the sign
+ * encoding are this library's stated reading):
+ *   - Codes: row-major [rows][K * bits / 32] int32 words; the code for K index
+ *     j*(32/bits)+i is bits [i*bits, (i+1)*bits) of word j, stored as
+ *     q + 2^(bits-1) (so q lies in [-2^(bits-1), 2^(bits-1)-1]).
+ *   - Scales: row-major [rows][K / group] IEEE binary16.
+ *   - w13: rows = 2I, K = H; rows [0, I) gate (w1), rows [I, 2I) up (w3).
+ *   - w2:  rows = H,  K = I.
+ *   - SwiGLU: g' = min(g, clamp), u' = min(max(u, -clamp), clamp),
+ *             a = g' * sigmoid(alpha * g') * (u' + beta); clamp = +INFINITY
+ *             disables clamping.
+ */
+#ifndef MOE_WNA16_H
+#define MOE_WNA16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_WNA16_OK = 0,
+    MOE_WNA16_EINVAL = -1,      /* bad shape, null pointer, NaN parameter   */
+    MOE_WNA16_EUNSUPPORTED = -2,/* bits / group / shape outside the kernels */
+    MOE_WNA16_EALIGN = -3,      /* pointer not aligned as required          */
+    MOE_WNA16_EWORKSPACE = -4,  /* workspace smaller than workspace_size    */
+    MOE_WNA16_EARCH = -5,       /* current device is not gfx950             */
+    MOE_WNA16_EHIP = -6         /* a HIP runtime call or launch failed      */
+} moe_wna16_status;
+
+/* Quantization of one projection: bits in {2, 4}; group in {32, 64, 128}. */
+typedef struct {
+    int32_t bits;
+    int32_t group;
+} moe_wna16_qparams;
+
+/* Tiling chosen for a call (a pure function of the shapes; see moe_wna16_plan). */
+typedef struct {
+    int32_t block_m;        /* rows of (token, slot) pairs per tile: 16 or 64      */
+    int32_t max_tiles;      /* tile capacity the grid is sized for                  */
+    int32_t w13_variant;    /* 0: decode-shaped (16 rows, 8 waves), 1: prefill-shaped */
+    int32_t w2_variant;     /* same encoding for the down projection               */
+} moe_wna16_plan_t;
+
+/*
+ * Bytes of device workspace moe_wna16_forward needs for these sizes (any
+ * bits / group).  *bytes_out is a HOST pointer.  Returns EINVAL on bad sizes.
+ */
+int moe_wna16_workspace_size(int T, int H, int I, int E, int topk, size_t *bytes_out);
+
+/*
+ * Tiling moe_wna16_forward will use for these arguments.  *plan_out is a
+ * HOST pointer.  Returns the same status forward would return from its
+ * shape / parameter checks (no device query).
+ */
+int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
+                   moe_wna16_qparams q2, moe_wna16_plan_t *plan_out);
+
+/*
+ * The routed layer (see the top of this file).
+ *
+ *   x           [T, H] bf16, row-major                          16-byte aligned
+ *   topk_ids    [T, topk] int32, expert ids                      4-byte aligned
+ *   topk_w      [T, topk] float32 routing weights, used as given 4-byte aligned
+ *   w13_packed  [E, 2I, H*b13/32] int32                         16-byte aligned
+ *   w13_scales  [E, 2I, H/g13] fp16                              2-byte aligned
+ *   w2_packed   [E, H, I*b2/32] int32                           16-byte aligned
+ *   w2_scales   [E, H, I/g2] fp16                                2-byte aligned
+ *   out         [T, H] bf16, written (never read)               16-byte aligned
+ *   workspace   >= moe_wna16_workspace_size bytes               256-byte aligned
+ *
+ * Shapes: T >= 0 (T = 0 returns OK with no launch), 1 <= E <= 1024,
+ * 1 <= topk <= 64, H and I multiples of 128, each group dividing its K.
+ * alpha, beta must be finite; clamp must be > 0 (or +INFINITY), not NaN.
+ * The output is the FP32 sum rounded to BF16 (nearest even).  Summation
+ * order across a token's experts is unspecified (FP32 atomics).
+ */
+int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_w,
+                      const int32_t *w13_packed, const uint16_t *w13_scales,
+                      const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H, int I,
+                      int E, int topk, moe_wna16_qparams q13, moe_wna16_qparams q2, float alpha,
+                      float beta, float clamp, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_wna16_forward with per-kernel timing.  `events` is a HOST array of 8
+ * caller-created hipEvent_t; the four kernels of the layer (in order: routing
+ * and activation reorder, w13 + SwiGLU, w2 + scatter-add, BF16 convert) record
+ * events[2i] when kernel i starts and events[2i+1] when it ends, from the
+ * dispatch packets themselves (no extra packets on the stream).  Same checks
+ * and status codes as moe_wna16_forward, plus EINVAL for a NULL `events`.
+ */
+int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const float *topk_w,
+                               const int32_t *w13_packed, const uint16_t *w13_scales,
+                               const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H,
+                               int I, int E, int topk, moe_wna16_qparams q13,
+                               moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t *events);
+
+/*
+ * Expert-sorted tile layout of the T*topk (token, slot) pairs, pair index
+ * p = t*topk + j.  Bit-exact and deterministic:
+ *   expert_offsets[E+1]  exclusive prefix sum of each expert's pair count
+ *                        rounded up to a multiple of block_m
+ *   sorted_ids[]         slot expert_offsets[e] + r holds the r-th smallest p
+ *                        routed to e (stable); padding slots hold T*topk.
+ *                        Capacity: (T*topk/block_m + min(E, T*topk)) * block_m.
+ *   tile_expert[]        expert of each block_m-slot tile; capacity
+ *                        T*topk/block_m + min(E, T*topk)
+ *   inv_perm[T*topk]     slot of pair p, or -1 for an id outside [0, E)
+ *   num_tiles[1]         expert_offsets[E] / block_m
+ *   bad_ids[1]           number of ids outside [0, E)
+ * Entries past num_tiles*block_m (sorted_ids) and num_tiles (tile_expert) are
+ * left untouched.  block_m in [1, 1024]; E <= 1024; int32 buffers 4-byte
+ * aligned.  T = 0 writes expert_offsets = 0 and num_tiles = bad_ids = 0.
+ */
+int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
+                    int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
+                    int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids,
+                    hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *moe_wna16_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_WNA16_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library: it loads, exports every function include/moe_wna16.h
+declares, and rejects bad arguments on the host before any device call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import weight_only_bit_moe_amd as M
+from weight_only_bit_moe_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_wna16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_wna16_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        pytest.fail(f"{M.LIB_PATH} not built (python -m weight_only_bit_moe_amd.build)")
+    return M.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == sorted(M.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert M.moe_wna16_status_string(st) not in ("", "unknown status")
+    assert M.moe_wna16_status_string(99) == "unknown status"
+
+
+def test_workspace_size_monotone(lib):
+    a = M.moe_wna16_workspace_size(4, 4096, 2048, 256, 6)
+    b = M.moe_wna16_workspace_size(64, 4096, 2048, 256, 6)
+    c = M.moe_wna16_workspace_size(8192, 4096, 2048, 256, 8)
+    assert 0 < a < b < c
+    assert M.moe_wna16_workspace_size(0, 256, 128, 8, 2) > 0
+    with pytest.raises(M.MoeWna16Error):
+        M.moe_wna16_workspace_size(4, 100, 2048, 256, 6)
+
+
+def test_plan_picks_tiles_from_rows_per_expert(lib):
+    dec = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (2, 128), (2, 128))
+    pre = M.moe_wna16_plan(2048, 4096, 2048, 256, 6, (2, 128), (2, 128))
+    assert dec["block_m"] == 16 and dec["w13_variant"] == 0 and dec["max_tiles"] == 24 // 16 + 24
+    assert pre["block_m"] == 64 and pre["w2_variant"] == 1
+    assert pre["max_tiles"] == 2048 * 6 // 64 + 256
+
+
+NAN, INF = float("nan"), math.inf
+GOOD = dict(T=4, H=256, I=128, E=8, topk=2, q13=(4, 128), q2=(4, 128), alpha=1.0, beta=0.0,
+            clamp=INF)
+
+
+def call(ptrs=16, ws_bytes=1 << 30, ws_ptr=4096, **over):
+    a = dict(GOOD)
+    a.update(over)
+    p = ptrs
+    return M.moe_wna16_forward(p, p, p, p, p, p, p, a["T"], a["H"], a["I"], a["E"], a["topk"],
+                               a["q13"], a["q2"], a["alpha"], a["beta"], a["clamp"], p, ws_ptr,
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), Bd.EINVAL), (dict(H=0), Bd.EINVAL), (dict(E=0), Bd.EINVAL),
+    (dict(topk=0), Bd.EINVAL), (dict(alpha=NAN), Bd.EINVAL), (dict(beta=INF), Bd.EINVAL),
+    (dict(clamp=NAN), Bd.EINVAL), (dict(clamp=-1.0), Bd.EINVAL),
+    (dict(q13=(3, 128)), Bd.EUNSUPPORTED), (dict(q2=(4, 96)), Bd.EUNSUPPORTED),
+    (dict(H=200), Bd.EUNSUPPORTED), (dict(I=64), Bd.EUNSUPPORTED), (dict(E=1025), Bd.EUNSUPPORTED),
+    (dict(topk=65), Bd.EUNSUPPORTED), (dict(I=128, q2=(2, 128)), None),
+])
+def test_forward_rejects_before_device(lib, over, status):
+    st = call(**over)
+    if status is None:   # valid arguments reach the device check (no GPU here)
+        assert st in (Bd.EHIP, Bd.EARCH, Bd.OK)
+    else:
+        assert st == status
+
+
+def test_forward_null_misaligned_and_workspace(lib):
+    assert call(ptrs=0) == Bd.EINVAL
+    assert call(ptrs=18) == Bd.EALIGN
+    assert call(ws_ptr=4096 + 16) == Bd.EALIGN
+    assert call(ws_bytes=10) == Bd.EWORKSPACE
+    need = M.moe_wna16_workspace_size(4, 256, 128, 8, 2)
+    assert call(ws_bytes=need - 1) == Bd.EWORKSPACE
+    assert call(ws_bytes=need) in (Bd.EHIP, Bd.EARCH, Bd.OK)
+
+
+def test_empty_batch_is_ok_without_device(lib):
+    assert call(T=0, ptrs=0, ws_ptr=0, ws_bytes=0) == Bd.OK
+
+
+def test_align_rejects(lib):
+    f = M.moe_wna16_align
+    assert f(16, 4, 2, 0, 16, 16, 16, 16, 16, 16, 16, None) == Bd.EINVAL
+    assert f(16, 4, 2, 8, 0, 16, 16, 16, 16, 16, 16, None) == Bd.EINVAL
+    assert f(16, 4, 2, 2048, 16, 16, 16, 16, 16, 16, 16, None) == Bd.EUNSUPPORTED
+    assert f(18, 4, 2, 8, 16, 16, 16, 16, 16, 16, 16, None) == Bd.EALIGN
+    assert f(0, 4, 2, 8, 16, 16, 16, 16, 16, 16, 16, None) == Bd.EINVAL
+
+
+def test_library_carries_gfx950_code_only(lib):
+    """The shared object embeds an offload bundle for gfx950 (our own build)."""
+    blob = open(M.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in blob

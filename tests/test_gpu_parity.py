@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Alignment outputs must match bit for bit.  The layer output must satisfy
+|gpu - oracle| <= 2e-2 * rms(oracle) + 1e-3 elementwise (rms over all compared
+elements).  Shapes straddle every tiling threshold: 16- and 64-row tiles,
+experts with 15/16/17 and 64/65 rows, K chunks of 128/256/512, W2/W4 with
+group 32/64/128 on each projection, empty experts, invalid and duplicate ids.
+The four full-size workloads run in the same launch configuration as the
+benchmark and are checked on tokens the oracle computes one by one.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import weight_only_bit_moe_amd as M
+from oracle import oracle as O
+from tests import _gpu as G
+from weight_only_bit_moe_amd.inputs import CONFIGS, LayerSpec, make_config, make_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return G.device()
+
+
+# --------------------------------------------------------------------------
+# alignment: bit-exact
+# --------------------------------------------------------------------------
+
+def gpu_align(ids_np, E, bm, dev):
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(dev)
+    r = M.align(ids, E, bm)
+    torch.cuda.synchronize(dev)
+    n = int(r["num_tiles"][0])
+    P = ids_np.size
+    return dict(sorted_ids=r["sorted_ids"][: n * bm].cpu().numpy(),
+                tile_expert=r["tile_expert"][:n].cpu().numpy(),
+                expert_offsets=r["expert_offsets"].cpu().numpy(),
+                inv_perm=r["inv_perm"][:P].cpu().numpy(), num_tiles=n,
+                bad_ids=int(r["bad_ids"][0]))
+
+
+def assert_align_equal(got, ref):
+    assert got["num_tiles"] == ref["num_tiles"]
+    assert got["bad_ids"] == ref["bad_ids"]
+    for k in ("sorted_ids", "tile_expert", "expert_offsets", "inv_perm"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def _align_cases():
+    cases = []
+    rng = np.random.default_rng(1234)
+    for i in range(12):
+        T = int(rng.integers(1, 3000))
+        k = int(rng.integers(1, 9))
+        E = int(rng.choice([1, 3, 8, 64, 256, 1000, 1024]))
+        cases.append((f"fuzz{i}", rng.integers(0, E, size=(T, k)), E))
+    ids = rng.integers(-3, 20, size=(300, 4))           # invalid ids mixed in
+    cases.append(("bad_ids", ids, 16))
+    cases.append(("one_hot_expert", np.full((1500, 2), 7), 256))
+    cases.append(("max_experts", rng.integers(0, 1024, size=(4096, 8)), 1024))
+    return cases
+
+
+@pytest.mark.parametrize("bm", [1, 16, 64, 128])
+@pytest.mark.parametrize("case", range(len(_align_cases())))
+def test_align_bit_exact(dev, case, bm):
+    name, ids, E = _align_cases()[case]
+    assert_align_equal(gpu_align(ids, E, bm, dev), O.align(ids, E, bm))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_align_bit_exact_on_workload_routing(dev, cfg):
+    sp = CONFIGS[cfg]
+    ids = make_layer(sp.replace(H=128, I=128, E=sp.E), cfg).topk_ids   # same routing draw
+    bm = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                          (sp.bits2, sp.group2))["block_m"]
+    assert_align_equal(gpu_align(ids, sp.E, bm, dev), O.align(ids, sp.E, bm))
+
+
+def test_align_empty_batch(dev):
+    got = gpu_align(np.zeros((0, 4), np.int32), 8, 16, dev)
+    assert got["num_tiles"] == 0 and not got["expert_offsets"].any()
+
+
+def test_align_deterministic(dev):
+    ids = np.random.default_rng(5).integers(0, 256, size=(2048, 6))
+    first = gpu_align(ids, 256, 64, dev)
+    for _ in range(20):
+        assert_align_equal(gpu_align(ids, 256, 64, dev), first)
+
+
+# --------------------------------------------------------------------------
+# the layer at sizes the oracle computes in full
+# --------------------------------------------------------------------------
+
+def spec(**kw):
+    base = dict(name="case", T=8, H=256, I=128, E=8, topk=2, bits13=4, group13=128, bits2=4,
+                group2=128, scale_lo=0.005, scale_hi=0.02)
+    base.update(kw)
+    return LayerSpec(**base)
+
+
+ACT = dict(alpha=1.702, beta=1.0, clamp=7.0)
+SMALL = {
+    "tiny_config": (CONFIGS[1], None, 0),
+    "w2_g128_g64_kc512": (spec(T=16, H=512, I=256, topk=4, bits13=2, bits2=2, group2=64,
+                               scale_lo=0.01, scale_hi=0.05, **ACT), None, 0),
+    "w4g32_w2g32_clamp_binds": (spec(T=24, H=384, I=512, E=6, topk=3, group13=32, bits2=2,
+                                     group2=32, alpha=1.702, beta=1.0, clamp=0.5), None, 0),
+    "w2g32_w4g64": (spec(T=12, H=256, I=256, E=5, topk=2, bits13=2, group13=32, bits2=4,
+                         group2=64), None, 0),
+    "prefill_zipf_multi_tile": (spec(T=256, H=256, I=256, E=8, topk=2, group13=64,
+                                     routing="zipf", **ACT), None, 1),
+    "prefill_65_rows_per_expert": (spec(T=130, H=384, I=128, E=4, topk=2), "65each", 1),
+    "prefill_w2g64_outliers": (spec(T=200, H=512, I=256, E=8, topk=4, bits13=4, bits2=2,
+                                    group2=64, routing="zipf", scale_dist="loguniform",
+                                    scale_lo=1e-3, scale_hi=5e-2, x_sigma=2.0,
+                                    outlier_frac=0.01, **ACT), None, 1),
+    "decode_15_16_17_rows": (spec(T=40, H=256, I=128, E=8, topk=2), "151617", 0),
+    "single_expert_single_slot": (spec(T=5, E=1, topk=1), None, 0),
+    "threshold_bm64_exact": (spec(T=64, H=256, I=128, E=4, topk=1), None, 1),
+}
+
+
+def forced_ids(kind, sp):
+    T, k, E = sp.T, sp.topk, sp.E
+    if kind == "65each":           # 4 experts x 65 pairs: 64-row tile + 1-row tail
+        flat = np.repeat(np.arange(E), T * k // E)
+        return np.random.default_rng(0).permutation(flat).reshape(T, k).astype(np.int32)
+    if kind == "151617":           # experts 0/1/2 get 17/16/15 pairs, 3 empty, rest spread
+        flat = np.concatenate([np.full(17, 0), np.full(16, 1), np.full(15, 2),
+                               np.arange(T * k - 48) % 4 + 4])
+        ids = np.random.default_rng(1).permutation(flat).reshape(T, k)
+        # keep ids distinct per token where possible
+        return ids.astype(np.int32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_matches_oracle(dev, name):
+    sp, forced, variant = SMALL[name]
+    L = make_layer(sp, seed=zlib.crc32(name.encode()) % 1000)
+    if forced:
+        L.topk_ids = forced_ids(forced, sp)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                            (sp.bits2, sp.group2))
+    assert plan["w13_variant"] == variant and plan["w2_variant"] == variant
+    got = G.to_f64(G.run_layer(L, dev))
+    ref = O.forward_layer(L)
+    G.assert_parity(got, ref, name)
+
+
+def test_layer_empty_experts_invalid_and_duplicate_ids(dev):
+    sp = spec(T=10, topk=3, E=8)
+    L = make_layer(sp, seed=77)
+    ids = L.topk_ids.copy()
+    ids[0, 1] = -1
+    ids[1, 2] = 8          # == E: out of range
+    ids[2, 0] = 1000
+    ids[3, 1] = ids[3, 0]  # duplicate within a token
+    ids[ids == 5] = 6      # expert 5 empty
+    L.topk_ids = ids.astype(np.int32)
+    got = G.to_f64(G.run_layer(L, dev))
+    G.assert_parity(got, O.forward_layer(L), "edge ids")
+
+
+def test_layer_empty_batch(dev):
+    L = make_layer(spec(T=0), seed=1)
+    y = G.run_layer(L, dev)
+    assert tuple(y.shape) == (0, 256)
+
+
+def test_swapped_gate_up_halves_would_fail(dev):
+    """The fused w13 keeps gate rows first; an oracle fed the halves swapped
+    must disagree with the library by more than the tolerance."""
+    sp = spec(T=16, H=256, I=128, topk=2, **ACT)
+    L = make_layer(sp, seed=9)
+    got = G.to_f64(G.run_layer(L, dev))
+    G.assert_parity(got, O.forward_layer(L), "true layout")
+    I = sp.I
+    Ls = make_layer(sp, seed=9)
+    Ls.w13 = np.concatenate([L.w13[:, I:], L.w13[:, :I]], axis=1).copy()
+    Ls.s13 = np.concatenate([L.s13[:, I:], L.s13[:, :I]], axis=1).copy()
+    assert G.parity_ratio(got, O.forward_layer(Ls)) > 1.0
+
+
+def test_repeat_runs_stay_within_tolerance(dev):
+    sp = spec(T=64, H=512, I=256, E=8, topk=4)
+    L = make_layer(sp, seed=3)
+    d = G.to_device(L, dev)
+    ref = O.forward_layer(L)
+    outs = [G.to_f64(G.run_layer(L, dev, d)) for _ in range(4)]
+    for y in outs:
+        G.assert_parity(y, ref, "repeat")
+
+
+def test_reused_workspace_and_output(dev):
+    """A second call with a smaller batch on the same workspace and output
+    buffers is unaffected by the first."""
+    big = make_layer(spec(T=48, topk=2), seed=11)
+    small = make_layer(spec(T=6, topk=2), seed=12)
+    ws = M.workspace_for(48, 256, 128, 8, 2, dev)
+    out = torch.empty((48, 256), dtype=torch.bfloat16, device=dev)
+    G.run_layer(big, dev, workspace=ws, out=out)
+    y = G.run_layer(small, dev, workspace=ws, out=out[:6])
+    G.assert_parity(G.to_f64(y), O.forward_layer(small), "reuse")
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, sampled tokens
+# --------------------------------------------------------------------------
+
+SAMPLES = {2: [0, 1, 2, 3], 3: [0, 17, 40, 63], 4: [0, 511, 1024, 2047], 5: [0, 3000, 8191]}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_workload_sampled_tokens(dev, cfg):
+    L = make_config(cfg)
+    sp = L.spec
+    print(f"config {cfg} {sp.name}: T={sp.T} E={sp.E} k={sp.topk}", flush=True)
+    y = G.to_f64(G.run_layer(L, dev))
+    assert np.all(np.isfinite(y))
+    rows = SAMPLES[cfg]
+    ref = O.forward_layer(L, tokens=rows)
+    G.assert_parity(y[rows], ref, f"config {cfg}")

@@ -1,0 +1,292 @@
+// Host side of the C ABI declared in include/moe_wna16.h: argument checks,
+// workspace layout, tiling plan and the launch sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "launch.hpp"
+#include "moe_wna16.h"
+
+namespace {
+
+using wna16::LayerDims;
+using wna16::Workspace;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 64;
+constexpr int kMaxBlockM = 64;       // largest tile the forward may choose
+constexpr int kMinGroup = 32;        // sizing bound for the per-group bias arrays
+constexpr size_t kRegionAlign = 256;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool valid_qparams(moe_wna16_qparams q)
+{
+    return (q.bits == 2 || q.bits == 4) && (q.group == 32 || q.group == 64 || q.group == 128);
+}
+
+// Basic size checks shared by workspace sizing and forward.
+int check_sizes(int T, int H, int I, int E, int topk)
+{
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0)
+        return MOE_WNA16_EINVAL;
+    if (E > kMaxExperts || topk > kMaxTopk)
+        return MOE_WNA16_EUNSUPPORTED;
+    if (H % 128 != 0 || I % 128 != 0)
+        return MOE_WNA16_EUNSUPPORTED;
+    // every index the kernels form stays within int32
+    const long long P = (long long)T * topk;
+    const long long slots = P + (long long)kMaxBlockM * (E < P ? E : P);
+    if ((long long)T * H >= (1LL << 31) || slots * I >= (1LL << 31) || P >= (1LL << 30))
+        return MOE_WNA16_EUNSUPPORTED;
+    return MOE_WNA16_OK;
+}
+
+struct Layout {
+    size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, total;
+};
+
+Layout layout_of(int T, int H, int I, int E, int topk)
+{
+    const size_t P = (size_t)T * topk;
+    const size_t minEP = (size_t)E < P ? (size_t)E : P;
+    const size_t max_tiles = P / 16 + minEP + 1;       // block_m = 16 bound
+    const size_t max_slots = P + kMaxBlockM * minEP;   // covers every block_m <= 64
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes, kRegionAlign);
+        return at;
+    };
+    L.meta = take(2 * sizeof(int32_t));
+    L.offsets = take((size_t)(E + 1) * sizeof(int32_t));
+    L.sorted = take(max_slots * sizeof(int32_t));
+    L.tiles = take(max_tiles * sizeof(int32_t));
+    L.inv = take((P ? P : 1) * sizeof(int32_t));
+    L.xperm = take((size_t)T * H * sizeof(uint16_t));
+    L.xbias = take((size_t)T * (H / kMinGroup) * sizeof(float));
+    L.act = take(max_slots * (size_t)I * sizeof(uint16_t));
+    L.actbias = take(max_slots * (size_t)(I / kMinGroup) * sizeof(float));
+    L.outf32 = take((size_t)T * H * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+void make_plan(int T, int E, int topk, moe_wna16_plan_t *plan)
+{
+    const long long P = (long long)T * topk;
+    // Prefill-shaped tiles once an expert averages 16+ rows; the 64-row kernel
+    // skips MFMAs of empty 16-row slices, so lightly used experts in a skewed
+    // batch cost little extra.
+    const int bm = (P >= 16LL * E) ? 64 : 16;
+    plan->block_m = bm;
+    plan->max_tiles = (int)(P / bm + (E < P ? E : P));
+    plan->w13_variant = bm == 64 ? 1 : 0;
+    plan->w2_variant = bm == 64 ? 1 : 0;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_WNA16_EHIP;
+    if (dev < 0 || dev >= 64)
+        return MOE_WNA16_EARCH;
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return MOE_WNA16_EHIP;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? MOE_WNA16_OK : MOE_WNA16_EARCH;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_WNA16_OK : MOE_WNA16_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_wna16_status_string(int status)
+{
+    switch (status) {
+    case MOE_WNA16_OK: return "ok";
+    case MOE_WNA16_EINVAL: return "invalid argument (shape, null pointer or NaN parameter)";
+    case MOE_WNA16_EUNSUPPORTED:
+        return "unsupported configuration (bits must be 2 or 4, group 32/64/128 dividing K, "
+               "H and I multiples of 128, E <= 1024, topk <= 64)";
+    case MOE_WNA16_EALIGN: return "misaligned pointer";
+    case MOE_WNA16_EWORKSPACE: return "workspace too small";
+    case MOE_WNA16_EARCH: return "current device is not gfx950 (MI355X)";
+    case MOE_WNA16_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int moe_wna16_workspace_size(int T, int H, int I, int E, int topk, size_t *bytes_out)
+{
+    if (!bytes_out)
+        return MOE_WNA16_EINVAL;
+    const int st = check_sizes(T, H, I, E, topk);
+    if (st != MOE_WNA16_OK)
+        return st;
+    *bytes_out = layout_of(T, H, I, E, topk).total;
+    return MOE_WNA16_OK;
+}
+
+int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
+                   moe_wna16_qparams q2, moe_wna16_plan_t *plan_out)
+{
+    if (!plan_out)
+        return MOE_WNA16_EINVAL;
+    int st = check_sizes(T, H, I, E, topk);
+    if (st != MOE_WNA16_OK)
+        return st;
+    if (!valid_qparams(q13) || !valid_qparams(q2) || H % q13.group || I % q2.group)
+        return MOE_WNA16_EUNSUPPORTED;
+    make_plan(T, E, topk, plan_out);
+    return MOE_WNA16_OK;
+}
+
+static int forward_impl(const void *x, const int32_t *topk_ids, const float *topk_w,
+                      const int32_t *w13_packed, const uint16_t *w13_scales,
+                      const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H, int I,
+                      int E, int topk, moe_wna16_qparams q13, moe_wna16_qparams q2, float alpha,
+                      float beta, float clamp, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream,
+                        const hipEvent_t *events)
+{
+    int st = check_sizes(T, H, I, E, topk);
+    if (st != MOE_WNA16_OK)
+        return st;
+    if (!std::isfinite(alpha) || !std::isfinite(beta) || std::isnan(clamp) || !(clamp > 0.f))
+        return MOE_WNA16_EINVAL;
+    if (!valid_qparams(q13) || !valid_qparams(q2) || H % q13.group || I % q2.group)
+        return MOE_WNA16_EUNSUPPORTED;
+    if (T == 0)
+        return MOE_WNA16_OK;
+    if (!x || !topk_ids || !topk_w || !w13_packed || !w13_scales || !w2_packed || !w2_scales ||
+        !out || !workspace)
+        return MOE_WNA16_EINVAL;
+    if (!aligned(x, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16) ||
+        !aligned(out, 16) || !aligned(workspace, kRegionAlign) || !aligned(topk_ids, 4) ||
+        !aligned(topk_w, 4) || !aligned(w13_scales, 2) || !aligned(w2_scales, 2))
+        return MOE_WNA16_EALIGN;
+    const Layout L = layout_of(T, H, I, E, topk);
+    if (workspace_bytes < L.total)
+        return MOE_WNA16_EWORKSPACE;
+    st = check_device();
+    if (st != MOE_WNA16_OK)
+        return st;
+
+    moe_wna16_plan_t plan;
+    make_plan(T, E, topk, &plan);
+    LayerDims d{};
+    d.T = T;
+    d.H = H;
+    d.I = I;
+    d.E = E;
+    d.topk = topk;
+    d.bits13 = q13.bits;
+    d.g13 = q13.group;
+    d.bits2 = q2.bits;
+    d.g2 = q2.group;
+    d.block_m = plan.block_m;
+    d.max_tiles = plan.max_tiles;
+    d.variant13 = plan.w13_variant;
+    d.variant2 = plan.w2_variant;
+    d.alpha = alpha;
+    d.beta = beta;
+    d.clamp = clamp;
+
+    char *base = static_cast<char *>(workspace);
+    Workspace ws{};
+    ws.meta = reinterpret_cast<int32_t *>(base + L.meta);
+    ws.expert_offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    ws.sorted_ids = reinterpret_cast<int32_t *>(base + L.sorted);
+    ws.tile_expert = reinterpret_cast<int32_t *>(base + L.tiles);
+    ws.inv_perm = reinterpret_cast<int32_t *>(base + L.inv);
+    ws.x_perm = reinterpret_cast<uint16_t *>(base + L.xperm);
+    ws.x_bias = reinterpret_cast<float *>(base + L.xbias);
+    ws.act = reinterpret_cast<uint16_t *>(base + L.act);
+    ws.act_bias = reinterpret_cast<float *>(base + L.actbias);
+    ws.out_f32 = reinterpret_cast<float *>(base + L.outf32);
+
+    wna16::KernelEvents ev[4];
+    if (events)
+        for (int i = 0; i < 4; ++i)
+            ev[i] = wna16::KernelEvents{events[2 * i], events[2 * i + 1]};
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, ev[0]))) !=
+        MOE_WNA16_OK)
+        return st;
+    if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
+        MOE_WNA16_OK)
+        return st;
+    if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream, ev[2]))) !=
+        MOE_WNA16_OK)
+        return st;
+    return hip_status(wna16::launch_convert(ws.out_f32, static_cast<uint16_t *>(out),
+                                            (size_t)T * H, stream, ev[3]));
+}
+
+int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_w,
+                      const int32_t *w13_packed, const uint16_t *w13_scales,
+                      const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H, int I,
+                      int E, int topk, moe_wna16_qparams q13, moe_wna16_qparams q2, float alpha,
+                      float beta, float clamp, void *out, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    return forward_impl(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
+                        I, E, topk, q13, q2, alpha, beta, clamp, out, workspace, workspace_bytes,
+                        stream, nullptr);
+}
+
+int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const float *topk_w,
+                               const int32_t *w13_packed, const uint16_t *w13_scales,
+                               const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H,
+                               int I, int E, int topk, moe_wna16_qparams q13,
+                               moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t *events)
+{
+    if (!events)
+        return MOE_WNA16_EINVAL;
+    return forward_impl(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
+                        I, E, topk, q13, q2, alpha, beta, clamp, out, workspace, workspace_bytes,
+                        stream, events);
+}
+
+int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
+                    int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
+                    int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids, hipStream_t stream)
+{
+    if (T < 0 || topk <= 0 || E <= 0 || block_m <= 0)
+        return MOE_WNA16_EINVAL;
+    if (E > kMaxExperts || block_m > 1024 || (long long)T * topk >= (1LL << 30))
+        return MOE_WNA16_EUNSUPPORTED;
+    if ((T > 0 && (!topk_ids || !inv_perm || !sorted_ids || !tile_expert)) || !expert_offsets ||
+        !num_tiles || !bad_ids)
+        return MOE_WNA16_EINVAL;
+    if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(tile_expert, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(inv_perm, 4) || !aligned(num_tiles, 4) ||
+        !aligned(bad_ids, 4))
+        return MOE_WNA16_EALIGN;
+    const int st = check_device();
+    if (st != MOE_WNA16_OK)
+        return st;
+    return hip_status(wna16::launch_align(topk_ids, T, topk, E, block_m, sorted_ids, tile_expert,
+                                          expert_offsets, inv_perm, num_tiles, bad_ids, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,816 @@
+// gfx950 (CDNA4) kernels of the routed WNA16 MoE layer.
+//
+// Data flow of one forward call (all on the caller's stream):
+//   route    block 0: stable counting sort of the (token, slot) pairs into
+//            expert-contiguous tiles of block_m rows; other blocks: copy x into
+//            MFMA fragment order with a per-group bias term, and zero the FP32
+//            accumulator.
+//   w13      per (tile, 128 gate columns): gather the tile's token rows, stream
+//            packed codes straight from HBM into registers, unpack to biased
+//            BF16, 16x16x32 BF16 MFMA per K group, scale each group's partial
+//            product once in FP32, SwiGLU(alpha, beta, clamp) epilogue -> BF16
+//            act in fragment order plus its per-group bias term.
+//   w2       per (tile, 128 output columns): same GEMM over act; the epilogue
+//            adds routing_weight * y into out_f32 with FP32 atomics.
+//   convert  out_f32 -> BF16 (round to nearest even).
+//
+// Weight format (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What
+// changed"): signed b-bit codes, field i of word j = K index j*(32/b)+i,
+// stored as q + 2^(b-1); FP16 scale per K group.  The MFMA never sees q
+// directly: a field u becomes the BF16 number 128 + u with one shift, mask and
+// OR per two codes (0x4300 is BF16 128.0 and has seven zero mantissa bits).
+// Per row and group the operand is then q + c with c = 128 + 2^(b-1), so
+//   sum_k x_k q_k = sum_k x_k (q_k + c) - c * sum_k x_k,
+// and the MFMA chain of each group starts from -c * sum_k x_k (precomputed per
+// activation row and group) instead of zero.  Products are exact in FP32 and
+// the group result is multiplied by its FP16 scale once.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "layout.hpp"
+
+namespace wna16 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kAlignThreads = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // round to nearest even
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// ---------------------------------------------------------------------------
+// Stable expert sort of the pairs, one workgroup of 1024 threads.
+//
+// Pairs are taken in chunks of 1024 in index order.  Inside a chunk a pair's
+// rank among equal experts = (equal experts in earlier waves of the chunk) +
+// (equal experts in earlier lanes of its wave); the lane part comes from 11
+// ballots (one per bit of the expert id), the wave part from a per-wave,
+// per-expert count table in LDS.  A running per-expert fill carries the order
+// across chunks, so the result equals a stable counting sort.
+// ---------------------------------------------------------------------------
+struct AlignShared {
+    int cnt[kMaxExperts];
+    int off[kMaxExperts + 1];
+    int run[kMaxExperts];
+    int wsum[kAlignThreads / 64];
+    int bad;
+    uint8_t wcnt[kAlignThreads / 64][kMaxExperts];
+};
+
+__device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, int P, int E,
+                            int bm, int32_t *__restrict__ sorted_ids,
+                            int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
+                            int32_t *__restrict__ inv_perm, int32_t *__restrict__ num_tiles,
+                            int32_t *__restrict__ bad_ids)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = kAlignThreads / 64;
+    for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
+        sh.cnt[e] = 0;
+        sh.run[e] = 0;
+        for (int w = 0; w < NW; ++w)
+            sh.wcnt[w][e] = 0;
+    }
+    if (tid == 0)
+        sh.bad = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kAlignThreads) {
+        const int e = ids[p];
+        if (e >= 0 && e < E)
+            atomicAdd(&sh.cnt[e], 1);
+        else
+            atomicAdd(&sh.bad, 1);
+    }
+    __syncthreads();
+
+    // exclusive scan of the padded counts (one expert per thread)
+    const int padded = tid < E ? (sh.cnt[tid] + bm - 1) / bm * bm : 0;
+    int incl = padded;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += y;
+    }
+    if (lane == 63)
+        sh.wsum[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int v = sh.wsum[w];
+            sh.wsum[w] = acc;
+            acc += v;
+        }
+        sh.off[E] = acc;
+    }
+    __syncthreads();
+    if (tid < E)
+        sh.off[tid] = sh.wsum[wave] + incl - padded;
+    __syncthreads();
+    const int total = sh.off[E];
+    for (int e = tid; e <= E; e += kAlignThreads)
+        offsets[e] = sh.off[e];
+    if (tid == 0) {
+        *num_tiles = total / bm;
+        *bad_ids = sh.bad;
+    }
+    // tile experts and padding slots
+    for (int s = tid; s < total; s += kAlignThreads) {
+        int lo = 0, hi = E - 1;  // last e with off[e] <= s
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.off[mid] <= s)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        if (s % bm == 0)
+            tile_expert[s / bm] = lo;
+        if (s - sh.off[lo] >= sh.cnt[lo])
+            sorted_ids[s] = P;
+    }
+    // stable placement
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < P; base += kAlignThreads) {
+        const int p = base + tid;
+        const int e = p < P ? ids[p] : -1;
+        const bool ok = p < P && e >= 0 && e < E;
+        const int key = ok ? e : kMaxExperts;  // 11-bit key; invalid lanes share one key
+        uint64_t m = ~0ull;
+#pragma unroll
+        for (int bit = 0; bit < 11; ++bit) {
+            const uint64_t bb = __ballot((key >> bit) & 1);
+            m &= ((key >> bit) & 1) ? bb : ~bb;
+        }
+        const int rank = __popcll(m & below);
+        const bool leader = (m & below) == 0;
+        const int cw = __popcll(m);
+        if (ok && leader)
+            sh.wcnt[wave][e] = (uint8_t)cw;
+        __syncthreads();
+        if (ok) {
+            int before = 0;
+            for (int w = 0; w < wave; ++w)
+                before += sh.wcnt[w][e];
+            const int slot = sh.off[e] + sh.run[e] + before + rank;
+            sorted_ids[slot] = p;
+            inv_perm[p] = slot;
+        } else if (p < P) {
+            inv_perm[p] = -1;
+        }
+        __syncthreads();
+        if (ok && leader) {
+            atomicAdd(&sh.run[e], cw);  // leaders of several waves may share an expert
+            sh.wcnt[wave][e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t *__restrict__ ids, int P, int E, int bm, int32_t *__restrict__ sorted_ids,
+    int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ inv_perm, int32_t *__restrict__ num_tiles,
+    int32_t *__restrict__ bad_ids)
+{
+    __shared__ AlignShared sh;
+    align_block(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
+                bad_ids);
+}
+
+// ---------------------------------------------------------------------------
+// Route kernel: block 0 sorts the pairs; blocks [1, 1 + nprep) reorder x into
+// fragment order and compute c * (group sum) per (token, w13 group); the
+// remaining blocks zero the FP32 accumulator.
+// ---------------------------------------------------------------------------
+template <int BITS, int GS>
+__global__ __launch_bounds__(kAlignThreads) void route_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int T, int H, int topk,
+    int E, int bm, int nprep, Workspace ws)
+{
+    __shared__ AlignShared sh;
+    if (blockIdx.x == 0) {
+        align_block(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert, ws.expert_offsets,
+                    ws.inv_perm, ws.meta, ws.meta + 1);
+        return;
+    }
+    if ((int)blockIdx.x <= nprep) {
+        const int ngroups = H / GS;
+        const int gid = (blockIdx.x - 1) * kAlignThreads + threadIdx.x;
+        if (gid >= T * ngroups)
+            return;
+        const int t = gid / ngroups, G = gid % ngroups;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + (size_t)t * H + (size_t)G * GS);
+        uint32_t w[GS / 2];
+#pragma unroll
+        for (int q = 0; q < GS / 8; ++q) {
+            const u32x4_t v = src[q];
+            w[4 * q + 0] = v[0];
+            w[4 * q + 1] = v[1];
+            w[4 * q + 2] = v[2];
+            w[4 * q + 3] = v[3];
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < GS; ++k)
+            sum += bf16_to_f32((w[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS);
+#pragma unroll
+        for (int q = 0; q < GS / 8; ++q) {
+            u32x4_t o;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int k0 = frag_src(BITS, GS, q * 8 + 2 * h);
+                const int k1 = frag_src(BITS, GS, q * 8 + 2 * h + 1);
+                const uint32_t lo = (w[k0 >> 1] >> (16 * (k0 & 1))) & 0xffffu;
+                const uint32_t hi = (w[k1 >> 1] >> (16 * (k1 & 1))) & 0xffffu;
+                o[h] = lo | (hi << 16);
+            }
+            dst[q] = o;
+        }
+        ws.x_bias[(size_t)t * ngroups + G] = (float)code_bias(BITS) * sum;
+        return;
+    }
+    // zero the accumulator
+    const size_t n4 = (size_t)T * H / 4;
+    const size_t nzero_threads = (size_t)(gridDim.x - 1 - nprep) * kAlignThreads;
+    f32x4_t *o = reinterpret_cast<f32x4_t *>(ws.out_f32);
+    for (size_t i = (size_t)(blockIdx.x - 1 - nprep) * kAlignThreads + threadIdx.x; i < n4;
+         i += nzero_threads)
+        o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------
+// Grouped WNA16 GEMM.
+//
+// Workgroup = NW waves; tile rows BM = 16*MT (pairs of one expert); each wave
+// owns NT column subtiles of 16 (W13: NT gate subtiles and the NT matching up
+// subtiles).  Lane l: column c = l % 16 of each subtile, lane group g = l / 16.
+// Per K group the lane needs gs/4 codes of its row: the contiguous codes
+// [g*gs/4, (g+1)*gs/4) of that group (a 2-bit 32-group: half of dword g/2),
+// i.e. NDW dwords loaded with one 16/8/4-byte load straight into registers.
+// A (activation rows, already in fragment order) goes through LDS in chunks of
+// KC elements; codes and scales of chunk c+1 are loaded while chunk c runs.
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+    const uint16_t *a;        // W13: x_perm [T][K]; W2: act [slots][K]
+    const float *a_bias;      // W13: x_bias [T][K/gs]; W2: act_bias [slots][K/gs]
+    const uint32_t *codes;    // [E][rows][K*bits/32]
+    const uint16_t *scales;   // [E][rows][K/gs]
+    const int32_t *sorted_ids;
+    const int32_t *tile_expert;
+    const int32_t *num_tiles;
+    const float *topk_w;      // W2 epilogue
+    uint16_t *act_out;        // W13 epilogue
+    float *act_bias_out;      // W13 epilogue
+    float *out_f32;           // W2 epilogue
+    int K;                    // reduction length (H for w13, I for w2)
+    int N;                    // output columns (I gate columns for w13, H for w2)
+    int P, topk;
+    int bits_next, gs_next;   // W13 epilogue: format of the w2 operand
+    float alpha, beta, clamp;
+};
+
+template <int BITS, int GS>
+struct CodeTraits {
+    static constexpr int NDW = (GS * BITS / 128) > 0 ? GS * BITS / 128 : 1;
+    static constexpr int S = GS / 32;  // MFMA steps per group
+    // first dword of lane group g's codes inside group G
+    static __device__ __forceinline__ int dword_off(int G, int g)
+    {
+        return (G * GS + g * (GS / 4)) * BITS / 32;
+    }
+};
+
+template <int NDW>
+__device__ __forceinline__ void load_codes(uint32_t (&dst)[NDW], const uint32_t *p)
+{
+    if constexpr (NDW == 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+        dst[0] = v[0];
+        dst[1] = v[1];
+        dst[2] = v[2];
+        dst[3] = v[3];
+    } else if constexpr (NDW == 2) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
+        dst[0] = v[0];
+        dst[1] = v[1];
+    } else {
+        dst[0] = *p;
+    }
+}
+
+// Biased BF16 fragment (8 values, 128 + u) of MFMA step s.
+template <int BITS, int GS, int NDW>
+__device__ __forceinline__ bf16x8_t unpack(const uint32_t (&cw)[NDW], int s, int g)
+{
+    u32x4_t r;
+    if constexpr (BITS == 4) {
+        const uint32_t d = cw[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = ((d >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+    } else {
+        const uint32_t d = (GS == 32) ? (cw[0] >> (8 * (g & 1))) : (cw[s >> 1] >> (8 * (s & 1)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = ((d >> (2 * i)) & 0x00030003u) | 0x43004300u;
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ float swiglu(float g, float u, float alpha, float beta, float clamp)
+{
+    const float gc = fminf(g, clamp);
+    const float uc = fminf(fmaxf(u, -clamp), clamp);
+    return gc / (1.0f + __expf(-alpha * gc)) * (uc + beta);
+}
+
+template <int BITS, int GS, int MT, int NT, int NW, int KC, bool W13>
+struct Gemm {
+    static constexpr int BM = 16 * MT;
+    static constexpr int NB = W13 ? 2 * NT : NT;  // B subtiles per wave
+    static constexpr int BN = NW * NT * 16;       // output columns per workgroup
+    static constexpr int GPC = KC / GS;           // groups per chunk
+    static constexpr int NDW = CodeTraits<BITS, GS>::NDW;
+    static constexpr int S = CodeTraits<BITS, GS>::S;
+    static constexpr int LDS_STRIDE = KC + 8;     // bf16 elements; rows 16 B apart mod 256 B
+    static constexpr int NTHREADS = NW * 64;
+
+    struct Shared {
+        uint16_t a[BM * LDS_STRIDE];
+        float bias[BM * GPC];
+        float part[BM * (BN / 8)];
+        int row_src[BM];
+        int row_pair[BM];
+        int rows_real;
+    };
+
+    struct BBuf {
+        uint32_t q[NB][GPC][NDW];
+        float s[NB][GPC];
+    };
+
+    static __device__ __forceinline__ void load_b(BBuf &buf, const uint32_t *const *brow,
+                                                  const uint16_t *const *srow, int chunk, int g)
+    {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+            for (int G = 0; G < GPC; ++G) {
+                const int Gg = chunk * GPC + G;
+                load_codes<NDW>(buf.q[j][G], brow[j] + CodeTraits<BITS, GS>::dword_off(Gg, g));
+                buf.s[j][G] = f16_to_f32(srow[j][Gg]);
+            }
+        }
+    }
+
+    // A chunk held in registers between its global load and its LDS store.
+    static constexpr int PIECES = KC / 8;  // 16-byte pieces per row and chunk
+    static constexpr int MAXP = (BM * PIECES + NTHREADS - 1) / NTHREADS;
+    static constexpr int MAXB = (BM * GPC + NTHREADS - 1) / NTHREADS;
+    struct ABuf {
+        u32x4_t v[MAXP];
+        float bias[MAXB];
+    };
+
+    static __device__ __forceinline__ void load_a(ABuf &ra, const Shared &sh, const GemmArgs &args,
+                                                  int chunk, int rows_active, int tid)
+    {
+        const int ngroups = args.K / GS;
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int q = tid + k * NTHREADS;
+            ra.v[k] = u32x4_t{0u, 0u, 0u, 0u};
+            if (q < rows_active * PIECES) {
+                const int src = sh.row_src[q / PIECES];
+                if (src >= 0)
+                    ra.v[k] = *reinterpret_cast<const u32x4_t *>(
+                        args.a + (size_t)src * args.K + (size_t)chunk * KC + (q % PIECES) * 8);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < MAXB; ++k) {
+            const int q = tid + k * NTHREADS;
+            ra.bias[k] = 0.f;
+            if (q < rows_active * GPC) {
+                const int src = sh.row_src[q / GPC];
+                if (src >= 0)
+                    ra.bias[k] = args.a_bias[(size_t)src * ngroups + chunk * GPC + q % GPC];
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void store_a(Shared &sh, const ABuf &ra, int rows_active,
+                                                   int tid)
+    {
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int q = tid + k * NTHREADS;
+            if (q < rows_active * PIECES)
+                *reinterpret_cast<u32x4_t *>(&sh.a[(q / PIECES) * LDS_STRIDE + (q % PIECES) * 8]) =
+                    ra.v[k];
+        }
+#pragma unroll
+        for (int k = 0; k < MAXB; ++k) {
+            const int q = tid + k * NTHREADS;
+            if (q < rows_active * GPC)
+                sh.bias[q] = ra.bias[k];
+        }
+    }
+
+    static __device__ __forceinline__ void compute_chunk(const Shared &sh, const BBuf &buf,
+                                                         f32x4_t (&acc)[MT][NB], int mt_active,
+                                                         int c, int g)
+    {
+#pragma unroll
+        for (int G = 0; G < GPC; ++G) {
+            f32x4_t negb[MT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    negb[i][v] = -sh.bias[(16 * i + 4 * g + v) * GPC + G];
+            f32x4_t accg[MT][NB];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                bf16x8_t af[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    if (i < mt_active)
+                        af[i] = *reinterpret_cast<const bf16x8_t *>(
+                            &sh.a[(16 * i + c) * LDS_STRIDE + G * GS + (s * 4 + g) * 8]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const bf16x8_t bf = unpack<BITS, GS, NDW>(buf.q[j][G], s, g);
+#pragma unroll
+                    for (int i = 0; i < MT; ++i)
+                        if (i < mt_active)
+                            accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                af[i], bf, s == 0 ? negb[i] : accg[i][j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                if (i < mt_active)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            acc[i][j][v] = fmaf(buf.s[j][G], accg[i][j][v], acc[i][j][v]);
+        }
+    }
+
+    static __device__ void run(const GemmArgs &args)
+    {
+        __shared__ __align__(16) Shared sh;
+        const int b = blockIdx.x;
+        if (b >= *args.num_tiles)
+            return;
+        const int nb = blockIdx.y;
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int c = lane & 15, g = lane >> 4;
+        const int e = args.tile_expert[b];
+
+        if (tid < 64) {
+            int p = args.P;
+            if (tid < BM)
+                p = args.sorted_ids[b * BM + tid];
+            const bool real = tid < BM && p < args.P;
+            if (tid < BM) {
+                sh.row_pair[tid] = p;
+                sh.row_src[tid] = real ? (W13 ? p / args.topk : b * BM + tid) : -1;
+            }
+            const uint64_t m = __ballot(real);
+            if (tid == 0)
+                sh.rows_real = __popcll(m);
+        }
+        __syncthreads();
+        const int rows_real = sh.rows_real;
+        const int mt_active = (rows_real + 15) >> 4;
+        const int rows_active = mt_active * 16;
+
+        // this lane's B rows
+        const int nrows = W13 ? 2 * args.N : args.N;
+        const int kw = args.K * BITS / 32;
+        const int ngroups = args.K / GS;
+        const uint32_t *brow[NB];
+        const uint16_t *srow[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int jj = W13 ? (j % NT) : j;
+            int n = nb * BN + wave * NT * 16 + jj * 16 + c;
+            if (W13 && j >= NT)
+                n += args.N;  // up projection rows follow the gate rows
+            const size_t row = (size_t)e * nrows + n;
+            brow[j] = args.codes + row * kw;
+            srow[j] = args.scales + row * ngroups;
+        }
+
+        f32x4_t acc[MT][NB];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        // Software pipeline: chunk ch+1's activation and weight loads are in
+        // flight while chunk ch runs on the MFMAs.  Activation loads are issued
+        // before weight loads so that waiting for them never waits for HBM.
+        const int nchunks = args.K / KC;
+        ABuf ra;
+        BBuf b0, b1;
+        load_a(ra, sh, args, 0, rows_active, tid);
+        load_b(b0, brow, srow, 0, g);
+        for (int ch = 0; ch < nchunks; ch += 2) {
+            __syncthreads();
+            store_a(sh, ra, rows_active, tid);
+            __syncthreads();
+            if (ch + 1 < nchunks) {
+                load_a(ra, sh, args, ch + 1, rows_active, tid);
+                load_b(b1, brow, srow, ch + 1, g);
+            }
+            compute_chunk(sh, b0, acc, mt_active, c, g);
+            if (ch + 1 < nchunks) {
+                __syncthreads();
+                store_a(sh, ra, rows_active, tid);
+                __syncthreads();
+                if (ch + 2 < nchunks) {
+                    load_a(ra, sh, args, ch + 2, rows_active, tid);
+                    load_b(b0, brow, srow, ch + 2, g);
+                }
+                compute_chunk(sh, b1, acc, mt_active, c, g);
+            }
+        }
+
+        if constexpr (W13) {
+            epilogue_w13(sh, args, acc, b, nb, wave, c, g, rows_real, mt_active, tid);
+        } else {
+            // routing-weighted scatter-add into the FP32 accumulator
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                if (i >= mt_active)
+                    continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * g + v;
+                    if (r >= rows_real)
+                        continue;
+                    const int p = sh.row_pair[r];
+                    const int t = p / args.topk;
+                    const float w = args.topk_w[p];
+                    float *orow = args.out_f32 + (size_t)t * args.N;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const int n = nb * BN + wave * NT * 16 + j * 16 + c;
+                        unsafeAtomicAdd(orow + n, w * acc[i][j][v]);
+                    }
+                }
+            }
+        }
+    }
+
+    // SwiGLU on matching gate/up columns; BF16 act rows written in the w2
+    // fragment order together with c2 * (group sum of the rounded values).
+    static __device__ __forceinline__ void epilogue_w13(Shared &sh, const GemmArgs &args,
+                                                        const f32x4_t (&acc)[MT][NB], int b,
+                                                        int nb, int wave, int c, int g,
+                                                        int rows_real, int mt_active, int tid)
+    {
+        static_assert(BN <= KC, "act tile reuses the A staging buffer");
+        constexpr int ACT_STRIDE = LDS_STRIDE;
+        __syncthreads();  // all waves are done with the last A chunk
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i >= mt_active)
+                continue;
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float a =
+                        swiglu(acc[i][j][v], acc[i][NT + j][v], args.alpha, args.beta, args.clamp);
+                    sh.a[(16 * i + 4 * g + v) * ACT_STRIDE + wave * NT * 16 + j * 16 + c] =
+                        f32_to_bf16(a);
+                }
+        }
+        __syncthreads();
+        const int gs2 = args.gs_next, bits2 = args.bits_next;
+        constexpr int PIECES = BN / 8;
+        for (int q = tid; q < rows_real * PIECES; q += NTHREADS) {
+            const int r = q / PIECES, c8 = q % PIECES;
+            const int gl = (c8 * 8) / gs2, pos0 = (c8 * 8) % gs2;
+            u32x4_t o;
+            float sum = 0.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t lo =
+                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, pos0 + 2 * h)];
+                const uint32_t hi =
+                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, pos0 + 2 * h + 1)];
+                sum += bf16_to_f32(lo);
+                sum += bf16_to_f32(hi);
+                o[h] = lo | (hi << 16);
+            }
+            *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(b * BM + r) * args.N +
+                                         nb * BN + c8 * 8) = o;
+            sh.part[r * PIECES + c8] = sum;
+        }
+        __syncthreads();
+        const int gpb = BN / gs2;  // w2 groups per workgroup
+        const int per = gs2 / 8;
+        const int ngroups2 = args.N / gs2;
+        const float cb = (float)code_bias(bits2);
+        for (int q = tid; q < rows_real * gpb; q += NTHREADS) {
+            const int r = q / gpb, gl = q % gpb;
+            float sum = 0.f;
+            for (int k = 0; k < per; ++k)
+                sum += sh.part[r * PIECES + gl * per + k];
+            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * gpb + gl] = cb * sum;
+        }
+    }
+};
+
+template <int BITS, int GS, int MT, int NT, int NW, int KC, bool W13>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs args)
+{
+    Gemm<BITS, GS, MT, NT, NW, KC, W13>::run(args);
+}
+
+__global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restrict__ dst,
+                               size_t n4)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4)
+        return;
+    const f32x4_t v = reinterpret_cast<const f32x4_t *>(src)[i];
+    u32x2_t o;
+    o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    reinterpret_cast<u32x2_t *>(dst)[i] = o;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
+                        int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
+                        int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids,
+                        hipStream_t stream)
+{
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids,
+                       T * topk, E, block_m, sorted_ids, tile_expert, expert_offsets, inv_perm,
+                       num_tiles, bad_ids);
+    return hipGetLastError();
+}
+
+template <int BITS, int GS>
+static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims &d,
+                          const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
+{
+    const long nthreads_prep = (long)d.T * (d.H / GS);
+    const int nprep = (int)((nthreads_prep + kAlignThreads - 1) / kAlignThreads);
+    const long n4 = (long)d.T * d.H / 4;
+    long nzero = (n4 + 4L * kAlignThreads - 1) / (4L * kAlignThreads);
+    if (nzero < 1)
+        nzero = 1;
+    if (nzero > 1024)
+        nzero = 1024;
+    hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(1 + nprep + (int)nzero),
+                          dim3(kAlignThreads), 0, stream, ev.start, ev.stop, 0, x, ids, d.T, d.H,
+                          d.topk, d.E, d.block_m, nprep, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerDims &d,
+                        const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
+{
+    const int key = d.bits13 * 1000 + d.g13;
+    switch (key) {
+    case 2032: return route_t<2, 32>(x, topk_ids, d, ws, stream, ev);
+    case 2064: return route_t<2, 64>(x, topk_ids, d, ws, stream, ev);
+    case 2128: return route_t<2, 128>(x, topk_ids, d, ws, stream, ev);
+    case 4032: return route_t<4, 32>(x, topk_ids, d, ws, stream, ev);
+    case 4064: return route_t<4, 64>(x, topk_ids, d, ws, stream, ev);
+    case 4128: return route_t<4, 128>(x, topk_ids, d, ws, stream, ev);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Tile shapes.  Variant 0 (few rows per expert, HBM-bound): 16-row tiles, 8
+// waves of one gate+up (or one output) subtile pair.  Variant 1 (many rows per
+// expert, MFMA-bound): 64-row tiles, 4 waves of 2 subtiles per projection half.
+template <int BITS, int GS, bool W13>
+static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, hipStream_t stream,
+                                const KernelEvents &ev)
+{
+    if (variant == 0) {
+        constexpr int NW = 8, MT = 1, NT = 1, BN = NW * NT * 16;
+        const dim3 grid(max_tiles, a.N / BN);
+        if (a.K % 512 == 0)
+            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 512, W13>), grid,
+                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 128, W13>), grid,
+                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+    } else {
+        constexpr int NW = 4, MT = 4, NT = 2, BN = NW * NT * 16;
+        const dim3 grid(max_tiles, a.N / BN);
+        if (a.K % 256 == 0)
+            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 256, W13>), grid,
+                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 128, W13>), grid,
+                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+    }
+    return hipGetLastError();
+}
+
+template <bool W13>
+static hipError_t gemm_select(const GemmArgs &a, int bits, int gs, int variant, int max_tiles,
+                              hipStream_t stream, const KernelEvents &ev)
+{
+    switch (bits * 1000 + gs) {
+    case 2032: return gemm_dispatch<2, 32, W13>(a, variant, max_tiles, stream, ev);
+    case 2064: return gemm_dispatch<2, 64, W13>(a, variant, max_tiles, stream, ev);
+    case 2128: return gemm_dispatch<2, 128, W13>(a, variant, max_tiles, stream, ev);
+    case 4032: return gemm_dispatch<4, 32, W13>(a, variant, max_tiles, stream, ev);
+    case 4064: return gemm_dispatch<4, 64, W13>(a, variant, max_tiles, stream, ev);
+    case 4128: return gemm_dispatch<4, 128, W13>(a, variant, max_tiles, stream, ev);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
+                      const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
+{
+    GemmArgs a{};
+    a.a = ws.x_perm;
+    a.a_bias = ws.x_bias;
+    a.codes = reinterpret_cast<const uint32_t *>(w13);
+    a.scales = s13;
+    a.sorted_ids = ws.sorted_ids;
+    a.tile_expert = ws.tile_expert;
+    a.num_tiles = ws.meta;
+    a.act_out = ws.act;
+    a.act_bias_out = ws.act_bias;
+    a.K = d.H;
+    a.N = d.I;
+    a.P = d.T * d.topk;
+    a.topk = d.topk;
+    a.bits_next = d.bits2;
+    a.gs_next = d.g2;
+    a.alpha = d.alpha;
+    a.beta = d.beta;
+    a.clamp = d.clamp;
+    return gemm_select<true>(a, d.bits13, d.g13, d.variant13, d.max_tiles, stream, ev);
+}
+
+hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
+                     const LayerDims &d, const Workspace &ws, hipStream_t stream,
+                     const KernelEvents &ev)
+{
+    GemmArgs a{};
+    a.a = ws.act;
+    a.a_bias = ws.act_bias;
+    a.codes = reinterpret_cast<const uint32_t *>(w2);
+    a.scales = s2;
+    a.sorted_ids = ws.sorted_ids;
+    a.tile_expert = ws.tile_expert;
+    a.num_tiles = ws.meta;
+    a.topk_w = topk_w;
+    a.out_f32 = ws.out_f32;
+    a.K = d.I;
+    a.N = d.H;
+    a.P = d.T * d.topk;
+    a.topk = d.topk;
+    return gemm_select<false>(a, d.bits2, d.g2, d.variant2, d.max_tiles, stream, ev);
+}
+
+hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,
+                          const KernelEvents &ev)
+{
+    const size_t n4 = n / 4;
+    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    hipExtLaunchKernelGGL(convert_kernel, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop,
+                          0, src, dst, n4);
+    return hipGetLastError();
+}
+
+}  // namespace wna16

@@ -1,0 +1,58 @@
+// Internal launchers of the gfx950 kernels (not part of the C ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace wna16 {
+
+// Device workspace regions of one forward call.
+struct Workspace {
+    int32_t *meta;            // [0] num_tiles, [1] bad ids
+    int32_t *expert_offsets;  // [E + 1]
+    int32_t *sorted_ids;      // [max_slots]
+    int32_t *tile_expert;     // [max_tiles]
+    int32_t *inv_perm;        // [P]
+    uint16_t *x_perm;         // [T, H] bf16, fragment order per w13 group
+    float *x_bias;            // [T, H / g13]
+    uint16_t *act;            // [max_slots, I] bf16, fragment order per w2 group
+    float *act_bias;          // [max_slots, I / g2]
+    float *out_f32;           // [T, H]
+};
+
+// Optional start/stop events recorded by the kernel dispatch itself
+// (hipExtLaunchKernelGGL); null events record nothing.
+struct KernelEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+struct LayerDims {
+    int T, H, I, E, topk;
+    int bits13, g13, bits2, g2;
+    int block_m, max_tiles, variant13, variant2;
+    float alpha, beta, clamp;
+};
+
+// Expert-sorted tiles + activation reorder/bias + zeroed accumulator.
+hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerDims &d,
+                        const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
+// Fused gate/up WNA16 GEMM with the SwiGLU epilogue.
+hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
+                      const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
+// Down WNA16 GEMM with the routing-weighted FP32 scatter-add epilogue.
+hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
+                     const LayerDims &d, const Workspace &ws, hipStream_t stream,
+                     const KernelEvents &ev);
+// FP32 accumulator -> BF16 output (round to nearest even).
+hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,
+                          const KernelEvents &ev);
+// Stand-alone tile layout (the moe_wna16_align entry point).
+hipError_t launch_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
+                        int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
+                        int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids,
+                        hipStream_t stream);
+
+}  // namespace wna16

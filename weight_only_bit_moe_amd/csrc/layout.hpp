@@ -1,0 +1,65 @@
+// Fragment order of the K dimension used by the WNA16 GEMM kernels.
+//
+// The GEMMs feed 16x16x32 BF16 MFMAs.  For one MFMA step every lane holds 8
+// consecutive K elements of its fragment; lane l (0..63) belongs to lane group
+// g = l / 16.  The packed weight codes are turned into BF16 two at a time with
+// one shift, one mask and one OR (see unpack in kernels.hip): a 4-bit word
+// yields the field pairs (i, i+4) and a 2-bit word the pairs (i, i+8).  Those
+// pairs are adjacent in the MFMA fragment, so the activation operand must list
+// its K elements in the same order.  Activations are therefore stored, inside
+// each quantization group of `gs` elements, at position
+//
+//     pos = (s * 4 + g) * 8 + v      (MFMA step s, lane group g, element v)
+//
+// holding in-group K offset frag_src(bits, gs, pos).  Every MFMA step stays
+// inside one group, so a group's partial product can be scaled once.
+#pragma once
+
+#if defined(__HIPCC__)
+#define WNA16_HD __host__ __device__ __forceinline__
+#else
+#define WNA16_HD inline
+#endif
+
+namespace wna16 {
+
+// In-group K offset stored at fragment position `pos` (0 <= pos < gs).
+WNA16_HD int frag_src(int bits, int gs, int pos)
+{
+    const int s = pos >> 5, g = (pos >> 3) & 3, v = pos & 7;
+    if (bits == 4)  // lane group g owns the gs/4 codes starting at g*gs/4; step s is its dword s
+        return g * (gs >> 2) + 8 * s + (v >> 1) + 4 * (v & 1);
+    if (gs == 32)   // 2-bit, one step per group: lane groups 2h, 2h+1 share dword h
+        return 16 * (g >> 1) + 4 * (g & 1) + (v >> 1) + 8 * (v & 1);
+    // 2-bit: step s reads half (s & 1) of dword (s >> 1) of the lane group's codes
+    return g * (gs >> 2) + 16 * (s >> 1) + 4 * (s & 1) + (v >> 1) + 8 * (v & 1);
+}
+
+// Inverse of frag_src: fragment position of in-group K offset `off`.
+WNA16_HD int frag_dst(int bits, int gs, int off)
+{
+    int g, s, v;
+    if (bits == 4) {
+        const int q = gs >> 2, r = off % q, r8 = r & 7;
+        g = off / q;
+        s = r >> 3;
+        v = 2 * (r8 & 3) + (r8 >> 2);
+    } else if (gs == 32) {
+        const int r16 = off & 15, r8 = r16 & 7;
+        g = 2 * (off >> 4) + (r8 >> 2);
+        s = 0;
+        v = 2 * (r8 & 3) + (r16 >> 3);
+    } else {
+        const int q = gs >> 2, r = off % q, r16 = r & 15, r8 = r16 & 7;
+        g = off / q;
+        s = 2 * (r >> 4) + (r8 >> 2);
+        v = 2 * (r8 & 3) + (r16 >> 3);
+    }
+    return (s * 4 + g) * 8 + v;
+}
+
+// Bias of the unpacked codes: a stored field u becomes the BF16 value 128 + u,
+// i.e. q + 128 + 2^(bits-1).
+WNA16_HD int code_bias(int bits) { return 128 + (1 << (bits - 1)); }
+
+}  // namespace wna16

@@ -35,6 +35,7 @@ __all__ = [
     "LayerSpec",
     "CONFIGS",
     "make_layer",
+    "make_batch",
     "make_config",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
@@ -162,28 +163,47 @@ def _scales(rng: np.random.Generator, spec: LayerSpec, shape) -> np.ndarray:
     return s.astype(np.float16)  # float64 -> float16, round to nearest even
 
 
+def _draw_batch(rng: np.random.Generator, spec: LayerSpec, outlier_channels=None):
+    """Draws 1-4 of the fixed order: routing ids, routing weights, x, outliers."""
+    T, H, k = spec.T, spec.H, spec.topk
+    ids = _routing_ids(rng, spec) if T > 0 else np.zeros((0, k), np.int32)
+    logits = rng.standard_normal((T, k))
+    if T > 0:
+        w = np.exp(logits - logits.max(axis=1, keepdims=True))
+        w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    else:
+        w = logits.astype(np.float32)
+    xf = (rng.standard_normal((T, H)) * spec.x_sigma).astype(np.float32)
+    n_out = int(round(spec.outlier_frac * H))
+    if n_out > 0:
+        drawn = np.sort(rng.choice(H, size=n_out, replace=False))
+        out_ch = drawn if outlier_channels is None else np.asarray(outlier_channels)
+        xf[:, out_ch] *= np.float32(spec.outlier_mult)
+    else:
+        out_ch = np.zeros(0, np.int64)
+    return ids, w, f32_to_bf16_bits(xf), out_ch.astype(np.int64)
+
+
+def make_batch(spec: LayerSpec, seed: int, outlier_channels=None):
+    """A fresh batch (topk_ids, topk_w, x) of the workload's distributions for an
+    existing layer; pass the layer's outlier channels to keep them fixed."""
+    ids, w, x, _ = _draw_batch(np.random.default_rng(seed), spec, outlier_channels)
+    return ids, w, x
+
+
 def make_layer(spec: LayerSpec, seed: int, topk_ids: Optional[np.ndarray] = None) -> Layer:
     """Draw one layer.  `topk_ids`, when given, replaces the routing draw
     (the routing-id draws are still made so the other arrays keep their bytes)."""
     T, H, I, E, k = spec.T, spec.H, spec.I, spec.E, spec.topk
     rng = np.random.default_rng(seed)
-    ids = _routing_ids(rng, spec) if T > 0 else np.zeros((0, k), np.int32)
+    ids, w, x, out_ch = _draw_batch(rng, spec)
     if topk_ids is not None:
         ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(T, k)
-    logits = rng.standard_normal((T, k))
-    w = np.exp(logits - logits.max(axis=1, keepdims=True)) if T > 0 else logits
-    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32) if T > 0 else w.astype(np.float32)
-    xf = (rng.standard_normal((T, H)) * spec.x_sigma).astype(np.float32)
-    n_out = int(round(spec.outlier_frac * H))
-    out_ch = np.sort(rng.choice(H, size=n_out, replace=False)) if n_out > 0 else np.zeros(0, np.int64)
-    if n_out:
-        xf[:, out_ch] *= np.float32(spec.outlier_mult)
-    x = f32_to_bf16_bits(xf)
     w13 = rng.integers(0, 2**32, size=(E, 2 * I, H * spec.bits13 // 32), dtype=np.uint32)
     s13 = _scales(rng, spec, (E, 2 * I, H // spec.group13))
     w2 = rng.integers(0, 2**32, size=(E, H, I * spec.bits2 // 32), dtype=np.uint32)
     s2 = _scales(rng, spec, (E, H, I // spec.group2))
-    return Layer(spec, x, ids, w, w13, s13, w2, s2, out_ch.astype(np.int64))
+    return Layer(spec, x, ids, w, w13, s13, w2, s2, out_ch)
 
 
 _BIG = dict(H=4096, I=2048, E=256)
