@@ -71,9 +71,10 @@ typedef struct {
 
 /* Tiling chosen for a call (a pure function of the shapes; see moe_wna16_plan). */
 typedef struct {
-    int32_t block_m;        /* rows of (token, slot) pairs per tile: 16 or 64      */
+    int32_t block_m;        /* rows of (token, slot) pairs per tile: 4 or 64        */
     int32_t max_tiles;      /* tile capacity the grid is sized for                  */
-    int32_t w13_variant;    /* 0: decode-shaped (16 rows, 8 waves), 1: prefill-shaped */
+    int32_t w13_variant;    /* 2: decode-shaped (4-row tiles, weight streaming),    */
+                            /* 1: prefill-shaped (64-row MFMA tiles)                */
     int32_t w2_variant;     /* same encoding for the down projection               */
 } moe_wna16_plan_t;
 
@@ -154,6 +155,16 @@ int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m
                     int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
                     int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids,
                     hipStream_t stream);
+
+/*
+ * Byte offset, inside the workspace of a moe_wna16_forward call with these
+ * sizes, of the FP32 accumulator [T, H] (row-major float) that holds the
+ * routed sum before its rounding to BF16.  It is valid once the call has
+ * completed and is overwritten by the next call on the same workspace; it
+ * lets a caller inspect the unrounded result.  *offset_out is a HOST pointer.
+ * Same size checks and status codes as moe_wna16_workspace_size.
+ */
+int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t *offset_out);
 
 /* Static description of a status code (never NULL). */
 const char *moe_wna16_status_string(int status);

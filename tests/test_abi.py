@@ -52,10 +52,15 @@ def test_workspace_size_monotone(lib):
 
 def test_plan_picks_tiles_from_rows_per_expert(lib):
     dec = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (2, 128), (2, 128))
+    bdec = M.moe_wna16_plan(64, 4096, 2048, 256, 6, (4, 128), (4, 128))
     pre = M.moe_wna16_plan(2048, 4096, 2048, 256, 6, (2, 128), (2, 128))
-    assert dec["block_m"] == 16 and dec["w13_variant"] == 0 and dec["max_tiles"] == 24 // 16 + 24
+    assert dec["block_m"] == 4 and dec["w13_variant"] == 2 and dec["max_tiles"] == 24 // 4 + 24
+    assert bdec["block_m"] == 4 and bdec["w2_variant"] == 2
     assert pre["block_m"] == 64 and pre["w2_variant"] == 1
     assert pre["max_tiles"] == 2048 * 6 // 64 + 256
+    # the decode kernel's LDS image must fit: a 32-group w13 at H=4096 goes prefill-shaped
+    big = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (4, 32), (2, 128))
+    assert big["w13_variant"] == 1
 
 
 NAN, INF = float("nan"), math.inf

@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe_wna16.so")
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP = 0, -1, -2, -3, -4, -5, -6
 
 #: every symbol include/moe_wna16.h declares
-EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_plan", "moe_wna16_forward",
-            "moe_wna16_forward_profiled", "moe_wna16_align", "moe_wna16_status_string")
+EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset", "moe_wna16_plan",
+            "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_align",
+            "moe_wna16_status_string")
 
 
 class QParams(ctypes.Structure):
@@ -54,6 +55,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     P, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_wna16_workspace_size.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
     lib.moe_wna16_workspace_size.restype = i
+    lib.moe_wna16_workspace_f32_offset.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.moe_wna16_workspace_f32_offset.restype = i
     lib.moe_wna16_plan.argtypes = [i, i, i, i, i, QParams, QParams, ctypes.POINTER(Plan)]
     lib.moe_wna16_plan.restype = i
     lib.moe_wna16_forward.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, QParams, QParams,
@@ -81,6 +84,21 @@ def moe_wna16_workspace_size(T: int, H: int, I: int, E: int, topk: int) -> int:
     if st != OK:
         raise MoeWna16Error(st, "moe_wna16_workspace_size")
     return out.value
+
+
+def moe_wna16_workspace_f32_offset(T: int, H: int, I: int, E: int, topk: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().moe_wna16_workspace_f32_offset(T, H, I, E, topk, ctypes.byref(out))
+    if st != OK:
+        raise MoeWna16Error(st, "moe_wna16_workspace_f32_offset")
+    return out.value
+
+
+def workspace_f32_sum(workspace, T, H, I, E, topk):
+    """View of the FP32 sum (before BF16 rounding) inside a forward's workspace."""
+    torch = _torch()
+    off = moe_wna16_workspace_f32_offset(T, H, I, E, topk)
+    return workspace[off: off + T * H * 4].view(torch.float32).view(T, H)
 
 
 def moe_wna16_plan(T, H, I, E, topk, q13: Tuple[int, int], q2: Tuple[int, int]) -> dict:

@@ -54,7 +54,7 @@ Layout layout_of(int T, int H, int I, int E, int topk)
 {
     const size_t P = (size_t)T * topk;
     const size_t minEP = (size_t)E < P ? (size_t)E : P;
-    const size_t max_tiles = P / 16 + minEP + 1;       // block_m = 16 bound
+    const size_t max_tiles = P / 4 + minEP + 1;        // smallest block_m (4) bound
     const size_t max_slots = P + kMaxBlockM * minEP;   // covers every block_m <= 64
     Layout L{};
     size_t o = 0;
@@ -77,17 +77,24 @@ Layout layout_of(int T, int H, int I, int E, int topk)
     return L;
 }
 
-void make_plan(int T, int E, int topk, moe_wna16_plan_t *plan)
+// Tiling: a pure function of the shapes.
+//   variant 2 (decode-shaped): 4-row tiles, whole-K activation rows in LDS,
+//     barrier-free weight streaming; used while experts average <= 4 rows and
+//     the LDS image fits 64 KB.
+//   variant 1 (prefill-shaped): 64-row tiles of 16x16x32 MFMAs; empty 16-row
+//     slices of a tile are skipped, so lightly used experts in a skewed batch
+//     cost little extra.
+void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
+               moe_wna16_qparams q2, moe_wna16_plan_t *plan)
 {
     const long long P = (long long)T * topk;
-    // Prefill-shaped tiles once an expert averages 16+ rows; the 64-row kernel
-    // skips MFMAs of empty 16-row slices, so lightly used experts in a skewed
-    // batch cost little extra.
-    const int bm = (P >= 16LL * E) ? 64 : 16;
+    const bool decode = P <= 4LL * E && wna16::decode_lds_bytes(H, q13.group) <= 65536 &&
+                        wna16::decode_lds_bytes(I, q2.group) <= 65536;
+    const int bm = decode ? wna16::kDecodeRows : 64;
     plan->block_m = bm;
     plan->max_tiles = (int)(P / bm + (E < P ? E : P));
-    plan->w13_variant = bm == 64 ? 1 : 0;
-    plan->w2_variant = bm == 64 ? 1 : 0;
+    plan->w13_variant = decode ? 2 : 1;
+    plan->w2_variant = decode ? 2 : 1;
 }
 
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
@@ -144,6 +151,17 @@ int moe_wna16_workspace_size(int T, int H, int I, int E, int topk, size_t *bytes
     return MOE_WNA16_OK;
 }
 
+int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t *offset_out)
+{
+    if (!offset_out)
+        return MOE_WNA16_EINVAL;
+    const int st = check_sizes(T, H, I, E, topk);
+    if (st != MOE_WNA16_OK)
+        return st;
+    *offset_out = layout_of(T, H, I, E, topk).outf32;
+    return MOE_WNA16_OK;
+}
+
 int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
                    moe_wna16_qparams q2, moe_wna16_plan_t *plan_out)
 {
@@ -154,7 +172,7 @@ int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
         return st;
     if (!valid_qparams(q13) || !valid_qparams(q2) || H % q13.group || I % q2.group)
         return MOE_WNA16_EUNSUPPORTED;
-    make_plan(T, E, topk, plan_out);
+    make_plan(T, H, I, E, topk, q13, q2, plan_out);
     return MOE_WNA16_OK;
 }
 
@@ -190,7 +208,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
         return st;
 
     moe_wna16_plan_t plan;
-    make_plan(T, E, topk, &plan);
+    make_plan(T, H, I, E, topk, q13, q2, &plan);
     LayerDims d{};
     d.T = T;
     d.H = H;

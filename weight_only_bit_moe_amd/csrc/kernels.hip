@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 template <int BITS, int GS>
 __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int T, int H, int topk,
-    int E, int bm, int nprep, Workspace ws)
+    int E, int bm, int nprep, size_t act_bias_n, Workspace ws)
 {
     __shared__ AlignShared sh;
     if (blockIdx.x == 0) {
@@ -247,13 +247,15 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         ws.x_bias[(size_t)t * ngroups + G] = (float)code_bias(BITS) * sum;
         return;
     }
-    // zero the accumulator
+    // zero the accumulator and the act bias terms (the decode epilogue adds into them)
     const size_t n4 = (size_t)T * H / 4;
     const size_t nzero_threads = (size_t)(gridDim.x - 1 - nprep) * kAlignThreads;
+    const size_t first = (size_t)(blockIdx.x - 1 - nprep) * kAlignThreads + threadIdx.x;
     f32x4_t *o = reinterpret_cast<f32x4_t *>(ws.out_f32);
-    for (size_t i = (size_t)(blockIdx.x - 1 - nprep) * kAlignThreads + threadIdx.x; i < n4;
-         i += nzero_threads)
+    for (size_t i = first; i < n4; i += nzero_threads)
         o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (size_t i = first; i < act_bias_n; i += nzero_threads)
+        ws.act_bias[i] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -653,6 +655,387 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs args)
     Gemm<BITS, GS, MT, NT, NW, KC, W13>::run(args);
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped grouped WNA16 GEMM ("stream" kernel).
+//
+// Tiles hold at most 4 (token, slot) rows, so the weight stream dominates
+// everything: each weight byte is used by <= 4 rows.  The whole K extent of
+// the tile's activation rows and the scales of the workgroup's weight rows go
+// to LDS once; after a single barrier every wave streams its own weight rows
+// with a rolling register pipeline (D load units of 16 rows x 64 bytes per
+// subtile in flight, no barrier until the epilogue).
+//
+// One load unit = dwords [16u, 16u+16) of a row: 256 codes (2-bit) or 128
+// (4-bit), i.e. U/gs whole groups.  Lane group g loads 16 contiguous bytes of
+// its row; v_permlane16/32_swap then regroup the dwords so that every lane
+// holds, for each group of the unit, the dwords its MFMA fragments need
+// (dwords [g*n, g*n + n) of the group with n = gs*bits/128).
+// ---------------------------------------------------------------------------
+template <int BITS, int GS, int NB, int D, bool W13>
+struct Stream {
+    static constexpr int R = 4;                      // rows per tile
+    static constexpr int NW = 4;                     // waves per workgroup
+    static constexpr int NTHREADS = NW * 64;
+    static constexpr int UK = 16 * 32 / BITS;        // K per load unit
+    static constexpr int GPU = UK / GS;              // groups per unit
+    static constexpr int S = GS / 32;                // MFMA steps per group
+    static constexpr bool SPLIT = (BITS == 2 && GS == 32);  // half a dword per lane and group
+    static constexpr int UDW = SPLIT ? 8 : 4;        // dwords a lane holds per unit and subtile
+    static constexpr int COLS = W13 ? NB / 2 * 16 : NB * 16;  // output columns per wave
+    static constexpr int BN = NW * COLS;             // output columns per workgroup
+
+    // dynamic LDS: A rows, their group bias terms, the workgroup's scales
+    static __host__ __device__ size_t lds_bytes(int K)
+    {
+        return (size_t)R * (K + 8) * 2 + (size_t)R * (K / GS) * 4 +
+               (size_t)NW * NB * 16 * (K / GS) * 2;
+    }
+
+    static __device__ __forceinline__ void load_unit(uint32_t (&dst)[NB][UDW],
+                                                     const uint32_t *const *brow, int u, int g)
+    {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const uint32_t *p = brow[j] + u * 16;
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    dst[j][q] = p[2 * q + (g >> 1)];
+            } else {
+                int off;
+                if constexpr (GPU == 2)
+                    off = 8 * (g & 1) + 4 * (g >> 1);
+                else
+                    off = 4 * g;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p + off);
+                dst[j][0] = v[0];
+                dst[j][1] = v[1];
+                dst[j][2] = v[2];
+                dst[j][3] = v[3];
+            }
+        }
+    }
+
+    // Regroup the loaded dwords across lane groups (see above).
+    static __device__ __forceinline__ void regroup(uint32_t (&r)[UDW])
+    {
+        if constexpr (!SPLIT && GPU == 2) {
+            const auto a = __builtin_amdgcn_permlane16_swap(r[0], r[2], false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(r[1], r[3], false, false);
+            r[0] = a[0];
+            r[2] = a[1];
+            r[1] = b[0];
+            r[3] = b[1];
+        } else if constexpr (!SPLIT && GPU == 4) {  // 4x4 transpose over lane groups
+            const auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+            const auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+            const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+            const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+            r[0] = c[0];
+            r[1] = c[1];
+            r[2] = d[0];
+            r[3] = d[1];
+        }
+    }
+
+    static __device__ __forceinline__ void take_unit(uint32_t (&r)[NB][UDW],
+                                                     const uint32_t (&qd)[NB][UDW])
+    {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+            for (int t = 0; t < UDW; ++t)
+                r[j][t] = qd[j][t];
+            regroup(r[j]);
+        }
+    }
+
+    // MFMAs of one load unit: for each of its groups, the biased-code products
+    // start from -c * (row group sum) and are scaled once by the group scale.
+    static __device__ __forceinline__ void compute_unit(const uint32_t (&r)[NB][UDW], int u,
+                                                        const uint16_t *sA, const float *sBias,
+                                                        const uint16_t *sSw, int lds_stride,
+                                                        int ngroups, int c, int g,
+                                                        f32x4_t (&acc)[NB])
+    {
+#pragma unroll
+        for (int gq = 0; gq < GPU; ++gq) {
+            const int G = u * GPU + gq;
+            f32x4_t negb;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float bv = sBias[v * ngroups + G];  // same address in every lane
+                negb[v] = g == 0 ? -bv : 0.f;
+            }
+            f32x4_t accg[NB];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(
+                    sA + (c < R ? c : 0) * lds_stride + G * GS + (s * 4 + g) * 8);
+                if (c >= R)
+                    af = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    uint32_t cw[4];
+                    if constexpr (SPLIT) {
+                        cw[0] = r[j][gq];
+                    } else if constexpr (GPU == 1) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            cw[t] = r[j][t];
+                    } else if constexpr (GPU == 2) {
+                        cw[0] = r[j][2 * gq];
+                        cw[1] = r[j][2 * gq + 1];
+                    } else {
+                        cw[0] = r[j][gq];
+                    }
+                    constexpr int NDW = CodeTraits<BITS, GS>::NDW;
+                    const bf16x8_t bf =
+                        unpack<BITS, GS, NDW>(reinterpret_cast<const uint32_t(&)[NDW]>(cw), s, g);
+                    accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf,
+                                                                      s == 0 ? negb : accg[j],
+                                                                      0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const float sc = f16_to_f32(sSw[(j * 16 + c) * ngroups + G]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[j][v] = fmaf(sc, accg[j][v], acc[j][v]);
+            }
+        }
+    }
+
+    static __device__ void run(const GemmArgs &args)
+    {
+        extern __shared__ __align__(16) unsigned char smem[];
+        const int b = blockIdx.x;
+        if (b >= *args.num_tiles)
+            return;
+        const int K = args.K;
+        const int ngroups = K / GS;
+        const int lds_stride = K + 8;
+        uint16_t *sA = reinterpret_cast<uint16_t *>(smem);
+        float *sBias = reinterpret_cast<float *>(smem + (size_t)R * lds_stride * 2);
+        uint16_t *sS = reinterpret_cast<uint16_t *>(smem + (size_t)R * lds_stride * 2 +
+                                                    (size_t)R * ngroups * 4);
+        __shared__ float s_part[R][NW * (W13 ? NB / 2 : 1)];
+
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int c = lane & 15, g = lane >> 4;
+        const int e = args.tile_expert[b];
+        const int nb = blockIdx.y;
+        // rows of the tile (uniform loads; padding rows have pair index P)
+        int src[R], pair[R];
+        int rows_real = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            pair[r] = args.sorted_ids[b * R + r];
+            const bool real = pair[r] < args.P;
+            src[r] = real ? (W13 ? pair[r] / args.topk : b * R + r) : -1;
+            rows_real += real ? 1 : 0;
+        }
+
+        // this lane's weight rows
+        const int nrows = W13 ? 2 * args.N : args.N;
+        const int kw = K * BITS / 32;
+        const uint32_t *brow[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            int n;
+            if constexpr (W13)
+                n = nb * BN + wave * COLS + (j % (NB / 2)) * 16 + c + (j >= NB / 2 ? args.N : 0);
+            else
+                n = nb * BN + wave * COLS + j * 16 + c;
+            brow[j] = args.codes + ((size_t)e * nrows + n) * kw;
+        }
+        const int nunits = K / UK;
+
+        // Activation rows (zero for padding rows), their bias terms and this
+        // workgroup's scales go to LDS first, in branch-free batches of loads.
+        {
+            const int k8n = K / 8;
+            const int apieces = R * k8n;
+            for (int i0 = 0; i0 < apieces; i0 += 4 * NTHREADS) {
+                u32x4_t v[4];
+                int at[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int i = i0 + t * NTHREADS + tid;
+                    const int ic = i < apieces ? i : apieces - 1;
+                    const int r = ic / k8n, k8 = ic % k8n;
+                    int sr = src[0];
+#pragma unroll
+                    for (int rr = 1; rr < R; ++rr)
+                        sr = r == rr ? src[rr] : sr;
+                    v[t] = *reinterpret_cast<const u32x4_t *>(args.a + (size_t)(sr >= 0 ? sr : 0) * K +
+                                                              k8 * 8);
+                    if (sr < 0)
+                        v[t] = u32x4_t{0u, 0u, 0u, 0u};
+                    at[t] = i < apieces ? r * lds_stride + k8 * 8 : -1;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (at[t] >= 0)
+                        *reinterpret_cast<u32x4_t *>(sA + at[t]) = v[t];
+            }
+            if (tid < R * ngroups || R * ngroups > NTHREADS) {
+                for (int i = tid; i < R * ngroups; i += NTHREADS) {
+                    const int r = i / ngroups;
+                    int sr = src[0];
+#pragma unroll
+                    for (int rr = 1; rr < R; ++rr)
+                        sr = r == rr ? src[rr] : sr;
+                    const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups + i % ngroups];
+                    sBias[i] = sr >= 0 ? bv : 0.f;
+                }
+            }
+            // scales of the workgroup's 16*NB*NW weight rows: row-contiguous runs
+            // of ngroups halves, copied 8 at a time when the run allows it
+            const int srows = NW * NB * 16;
+            if (ngroups % 8 == 0 && reinterpret_cast<uintptr_t>(args.scales) % 16 == 0) {
+                const int per = ngroups / 8;
+                const int spieces = srows * per;
+                for (int i0 = 0; i0 < spieces; i0 += 4 * NTHREADS) {
+                    u32x4_t v[4];
+                    int at[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int i = i0 + t * NTHREADS + tid;
+                        const int ic = i < spieces ? i : spieces - 1;
+                        const int rr = ic / per, k = ic % per;
+                        const int w = rr / (NB * 16), j = (rr / 16) % NB, cc = rr % 16;
+                        int n;
+                        if constexpr (W13)
+                            n = nb * BN + w * COLS + (j % (NB / 2)) * 16 + cc +
+                                (j >= NB / 2 ? args.N : 0);
+                        else
+                            n = nb * BN + w * COLS + j * 16 + cc;
+                        v[t] = *reinterpret_cast<const u32x4_t *>(
+                            args.scales + ((size_t)e * nrows + n) * ngroups + k * 8);
+                        at[t] = i < spieces ? rr * ngroups + k * 8 : -1;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (at[t] >= 0)
+                            *reinterpret_cast<u32x4_t *>(sS + at[t]) = v[t];
+                }
+            } else {
+                for (int i = tid; i < srows * ngroups; i += NTHREADS) {
+                    const int rr = i / ngroups, G = i % ngroups;
+                    const int w = rr / (NB * 16), j = (rr / 16) % NB, cc = rr % 16;
+                    int n;
+                    if constexpr (W13)
+                        n = nb * BN + w * COLS + (j % (NB / 2)) * 16 + cc +
+                            (j >= NB / 2 ? args.N : 0);
+                    else
+                        n = nb * BN + w * COLS + j * 16 + cc;
+                    sS[i] = args.scales[((size_t)e * nrows + n) * ngroups + G];
+                }
+            }
+        }
+        __syncthreads();
+        // the weight stream: D load units per subtile in flight from here on
+        uint32_t q[D][NB][UDW];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            load_unit(q[d], brow, d, g);
+
+        f32x4_t acc[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint16_t *sSw = sS + (size_t)wave * NB * 16 * ngroups;
+
+        // nunits is a multiple of D (checked by the host): the steady state
+        // reloads every slot unconditionally, the last round only drains.
+        int u0 = 0;
+        for (; u0 + D < nunits; u0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                uint32_t r[NB][UDW];
+                take_unit(r, q[d]);
+                load_unit(q[d], brow, u0 + d + D, g);
+                // keep the reload here: moving it later would drain the pipeline
+                __builtin_amdgcn_sched_barrier(0);
+                compute_unit(r, u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, acc);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            uint32_t r[NB][UDW];
+            take_unit(r, q[d]);
+            compute_unit(r, u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, acc);
+        }
+
+        // rows 0..3 of every subtile live in lane group 0, element v = row
+        if constexpr (W13) {
+            constexpr int NG = NB / 2;
+            const int gs2 = args.gs_next, bits2 = args.bits_next;
+            const int ngroups2 = args.N / gs2;
+            const float cb = (float)code_bias(bits2);
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                const int n = nb * BN + wave * COLS + j * 16 + c;  // gate column
+                const int G2 = n / gs2;
+                const int pos = G2 * gs2 + frag_dst(bits2, gs2, n % gs2);
+#pragma unroll
+                for (int v = 0; v < R; ++v) {
+                    float a = 0.f;
+                    if (g == 0 && v < rows_real) {
+                        a = swiglu(acc[j][v], acc[NG + j][v], args.alpha, args.beta, args.clamp);
+                        const uint16_t ab = f32_to_bf16(a);
+                        args.act_out[(size_t)(b * R + v) * args.N + pos] = ab;
+                        a = bf16_to_f32(ab);
+                    }
+                    // sum of the 16 columns of this subtile (lanes 0..15)
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1)
+                        a += __shfl_xor(a, m, 64);
+                    if (lane == 0)
+                        s_part[v][wave * NG + j] = a;
+                }
+            }
+            __syncthreads();
+            // one partial sum per (row, w2 group) inside this workgroup; a group
+            // wider than the workgroup gets two commutative contributions
+            const int per = gs2 >= 16 ? gs2 / 16 : 1;              // subtiles per group
+            const int nsub = NW * NG;                              // subtiles in the WG
+            const int gspan = nsub < per ? nsub : per;
+            for (int i = tid; i < rows_real * (nsub / gspan); i += NTHREADS) {
+                const int v = i / (nsub / gspan), k = i % (nsub / gspan);
+                float sum = 0.f;
+                for (int t = 0; t < gspan; ++t)
+                    sum += s_part[v][k * gspan + t];
+                const int G2 = (nb * BN + k * gspan * 16) / gs2;
+                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, cb * sum);
+            }
+        } else {
+            if (g == 0) {
+#pragma unroll
+                for (int v = 0; v < R; ++v) {
+                    if (v >= rows_real)
+                        continue;
+                    const int p = pair[v];
+                    const float w = args.topk_w[p];
+                    float *orow = args.out_f32 + (size_t)(p / args.topk) * args.N;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        unsafeAtomicAdd(orow + nb * BN + wave * COLS + j * 16 + c, w * acc[j][v]);
+                }
+            }
+        }
+    }
+};
+
+template <int BITS, int GS, int NB, int D, bool W13>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void stream_kernel(
+    const GemmArgs args)
+{
+    Stream<BITS, GS, NB, D, W13>::run(args);
+}
+
 __global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restrict__ dst,
                                size_t n4)
 {
@@ -694,7 +1077,8 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
         nzero = 1024;
     hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(1 + nprep + (int)nzero),
                           dim3(kAlignThreads), 0, stream, ev.start, ev.stop, 0, x, ids, d.T, d.H,
-                          d.topk, d.E, d.block_m, nprep, ws);
+                          d.topk, d.E, d.block_m, nprep,
+                          (size_t)d.max_tiles * d.block_m * (d.I / d.g2), ws);
     return hipGetLastError();
 }
 
@@ -713,22 +1097,27 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
     }
 }
 
-// Tile shapes.  Variant 0 (few rows per expert, HBM-bound): 16-row tiles, 8
-// waves of one gate+up (or one output) subtile pair.  Variant 1 (many rows per
-// expert, MFMA-bound): 64-row tiles, 4 waves of 2 subtiles per projection half.
+// Tile shapes.  Variant 2 (few rows per expert, HBM-bound): the stream kernel
+// on 4-row tiles.  Variant 1 (many rows per expert, MFMA-bound): 64-row tiles,
+// 4 waves of 2 subtiles per projection half.
 template <int BITS, int GS, bool W13>
 static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, hipStream_t stream,
                                 const KernelEvents &ev)
 {
-    if (variant == 0) {
-        constexpr int NW = 8, MT = 1, NT = 1, BN = NW * NT * 16;
-        const dim3 grid(max_tiles, a.N / BN);
-        if (a.K % 512 == 0)
-            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 512, W13>), grid,
-                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+    if (variant == 2) {
+        constexpr int NB = 2;
+        constexpr int D = Stream<BITS, GS, NB, 4, W13>::SPLIT ? 2 : 4;
+        using K_ = Stream<BITS, GS, NB, D, W13>;
+        using K1 = Stream<BITS, GS, NB, 1, W13>;
+        const dim3 grid(max_tiles, a.N / K_::BN);
+        if ((a.K / K_::UK) % D == 0)
+            hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, D, W13>), grid,
+                                  dim3(K_::NTHREADS), (uint32_t)K_::lds_bytes(a.K), stream,
+                                  ev.start, ev.stop, 0, a);
         else
-            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 128, W13>), grid,
-                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+            hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, 1, W13>), grid,
+                                  dim3(K1::NTHREADS), (uint32_t)K1::lds_bytes(a.K), stream,
+                                  ev.start, ev.stop, 0, a);
     } else {
         constexpr int NW = 4, MT = 4, NT = 2, BN = NW * NT * 16;
         const dim3 grid(max_tiles, a.N / BN);
@@ -801,6 +1190,14 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
     a.P = d.T * d.topk;
     a.topk = d.topk;
     return gemm_select<false>(a, d.bits2, d.g2, d.variant2, d.max_tiles, stream, ev);
+}
+
+size_t decode_lds_bytes(int K, int gs)
+{
+    // rows, their bias terms and the scales of 2 subtiles per wave (any bit width)
+    using S_ = Stream<2, 128, 2, 8, true>;
+    return (size_t)S_::R * (K + 8) * 2 + (size_t)S_::R * (K / gs) * 4 +
+           (size_t)S_::NW * 2 * 16 * (K / gs) * 2;
 }
 
 hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,

@@ -49,6 +49,10 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
 // FP32 accumulator -> BF16 output (round to nearest even).
 hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,
                           const KernelEvents &ev);
+// Dynamic LDS bytes of the decode-shaped GEMM for reduction length K, group gs.
+size_t decode_lds_bytes(int K, int gs);
+// Rows per tile of the decode-shaped GEMM.
+constexpr int kDecodeRows = 4;
 // Stand-alone tile layout (the moe_wna16_align entry point).
 hipError_t launch_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
                         int32_t *sorted_ids, int32_t *tile_expert, int32_t *expert_offsets,
