@@ -50,7 +50,22 @@ def parse():
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=None,
                     help="rocprofv3 counter summary holding the dominant kernel's HBM traffic")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times) "
+                         "and exit: the reference reading for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """Plain copy of a known size, for calibrating FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes": mib << 20, "repeats": 5}), flush=True)
 
 
 class Hip:
@@ -101,6 +116,9 @@ def kernel_traffic(path, kernel):
 
 def main():
     args = parse()
+    if args.copy_mib:
+        copy_probe(args.copy_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this layer has no multi-GPU path here "

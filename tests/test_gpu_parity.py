@@ -189,6 +189,17 @@ def test_layer_empty_experts_invalid_and_duplicate_ids(dev):
     G.assert_parity(got, O.forward_layer(L), "edge ids")
 
 
+@pytest.mark.parametrize("T,E", [(6, 8), (64, 4)])   # decode-shaped, prefill-shaped
+def test_token_without_valid_ids_gets_zero_output(dev, T, E):
+    sp = spec(T=T, topk=2, E=E)
+    L = make_layer(sp, seed=78)
+    L.topk_ids[1, :] = [-1, E]           # token 1: no valid id
+    L.topk_ids[3, 0] = -5                # token 3: one valid id left
+    y, got = G.run_layer(L, dev)
+    G.assert_parity(got, O.forward_layer(L), "no valid ids")
+    assert not G.to_f64(y)[1].any()
+
+
 def test_layer_empty_batch(dev):
     L = make_layer(spec(T=0), seed=1)
     y, _ = G.run_layer(L, dev)

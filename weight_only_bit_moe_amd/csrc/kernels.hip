@@ -53,6 +53,12 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h)
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
+// BF16 value `h` divided by 2^e (exact unless it underflows).
+__device__ __forceinline__ uint32_t bf16_scaled(uint32_t h, int e)
+{
+    return e == 0 ? h : f32_to_bf16(bf16_to_f32(h) * __builtin_ldexpf(1.0f, -e));
+}
+
 // ---------------------------------------------------------------------------
 // Stable expert sort of the pairs, one workgroup of 1024 threads.
 //
@@ -226,25 +232,26 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
             w[4 * q + 2] = v[2];
             w[4 * q + 3] = v[3];
         }
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < GS; ++k)
-            sum += bf16_to_f32((w[k >> 1] >> (16 * (k & 1))) & 0xffffu);
+        float sum = 0.f;  // sum of (stored activation) * (its bias weight)
         u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS);
 #pragma unroll
         for (int q = 0; q < GS / 8; ++q) {
             u32x4_t o;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const int k0 = frag_src(BITS, GS, q * 8 + 2 * h);
-                const int k1 = frag_src(BITS, GS, q * 8 + 2 * h + 1);
-                const uint32_t lo = (w[k0 >> 1] >> (16 * (k0 & 1))) & 0xffffu;
-                const uint32_t hi = (w[k1 >> 1] >> (16 * (k1 & 1))) & 0xffffu;
+                const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
+                const int k0 = frag_src(BITS, GS, p0), k1 = frag_src(BITS, GS, p1);
+                const uint32_t lo =
+                    bf16_scaled((w[k0 >> 1] >> (16 * (k0 & 1))) & 0xffffu, frag_shift(BITS, GS, p0));
+                const uint32_t hi =
+                    bf16_scaled((w[k1 >> 1] >> (16 * (k1 & 1))) & 0xffffu, frag_shift(BITS, GS, p1));
+                sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
+                sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
                 o[h] = lo | (hi << 16);
             }
             dst[q] = o;
         }
-        ws.x_bias[(size_t)t * ngroups + G] = (float)code_bias(BITS) * sum;
+        ws.x_bias[(size_t)t * ngroups + G] = sum;
         return;
     }
     // zero the accumulator and the act bias terms (the decode epilogue adds into them)
@@ -318,21 +325,60 @@ __device__ __forceinline__ void load_codes(uint32_t (&dst)[NDW], const uint32_t 
     }
 }
 
-// Biased BF16 fragment (8 values, 128 + u) of MFMA step s.
+// Constants of the code unpack held in registers the compiler cannot fold
+// (produced once by a volatile move), so that (x & mask) | magic is selected
+// as one v_and_or_b32: a VOP3 instruction cannot encode two literals.  The
+// unpack itself stays ordinary code, so the compiler's hazard rules (e.g. a
+// VALU write to an in-flight MFMA's accumulator input) still apply to it.
+struct UnpackConsts {
+    uint32_t magic;   // SGPR: BF16 128.0 in both halves
+    uint32_t m3, mc, m30, mf;  // VGPRs: 0x00030003, 0x000C000C, 0x00300030, 0x000F000F
+};
+
+__device__ __forceinline__ UnpackConsts unpack_consts()
+{
+    UnpackConsts k;
+    asm volatile("s_mov_b32 %0, 0x43004300" : "=s"(k.magic));
+    asm volatile("v_mov_b32 %0, 0x00030003" : "=v"(k.m3));
+    asm volatile("v_mov_b32 %0, 0x000c000c" : "=v"(k.mc));
+    asm volatile("v_mov_b32 %0, 0x00300030" : "=v"(k.m30));
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.mf));
+    return k;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic)
+{
+    return (x & mask) | magic;
+}
+
+// Biased BF16 fragment of MFMA step s: 4-bit fields give 128 + u; 2-bit
+// fields give 128 + m*u with the m of frag_shift (see layout.hpp).
 template <int BITS, int GS, int NDW>
-__device__ __forceinline__ bf16x8_t unpack(const uint32_t (&cw)[NDW], int s, int g)
+__device__ __forceinline__ bf16x8_t unpack(const uint32_t (&cw)[NDW], int s, int g,
+                                           const UnpackConsts &k)
 {
     u32x4_t r;
     if constexpr (BITS == 4) {
         const uint32_t d = cw[s];
+        r[0] = and_or(d, k.mf, k.magic);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r[i] = ((d >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+        for (int i = 1; i < 4; ++i)
+            r[i] = and_or(d >> (4 * i), k.mf, k.magic);
     } else {
-        const uint32_t d = (GS == 32) ? (cw[0] >> (8 * (g & 1))) : (cw[s >> 1] >> (8 * (s & 1)));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            r[i] = ((d >> (2 * i)) & 0x00030003u) | 0x43004300u;
+        const uint32_t d = (GS == 32) ? cw[0] : cw[s >> 1];
+        const int h = (GS == 32) ? (g & 1) : (s & 1);
+        if (h == 0) {  // field pairs 0, 1, 2 (word) and 3 (word >> 6)
+            r[0] = and_or(d, k.m3, k.magic);
+            r[1] = and_or(d, k.mc, k.magic);
+            r[2] = and_or(d, k.m30, k.magic);
+            r[3] = and_or(d >> 6, k.m3, k.magic);
+        } else {       // field pairs 4, 5 (word >> 6) and 6, 7 (word >> 12)
+            const uint32_t d6 = d >> 6, d12 = d >> 12;
+            r[0] = and_or(d6, k.mc, k.magic);
+            r[1] = and_or(d6, k.m30, k.magic);
+            r[2] = and_or(d12, k.m3, k.magic);
+            r[3] = and_or(d12, k.mc, k.magic);
+        }
     }
     return __builtin_bit_cast(bf16x8_t, r);
 }
@@ -439,7 +485,7 @@ struct Gemm {
 
     static __device__ __forceinline__ void compute_chunk(const Shared &sh, const BBuf &buf,
                                                          f32x4_t (&acc)[MT][NB], int mt_active,
-                                                         int c, int g)
+                                                         int c, int g, const UnpackConsts &magic)
     {
 #pragma unroll
         for (int G = 0; G < GPC; ++G) {
@@ -460,7 +506,7 @@ struct Gemm {
                             &sh.a[(16 * i + c) * LDS_STRIDE + G * GS + (s * 4 + g) * 8]);
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const bf16x8_t bf = unpack<BITS, GS, NDW>(buf.q[j][G], s, g);
+                    const bf16x8_t bf = unpack<BITS, GS, NDW>(buf.q[j][G], s, g, magic);
 #pragma unroll
                     for (int i = 0; i < MT; ++i)
                         if (i < mt_active)
@@ -536,6 +582,7 @@ struct Gemm {
         // flight while chunk ch runs on the MFMAs.  Activation loads are issued
         // before weight loads so that waiting for them never waits for HBM.
         const int nchunks = args.K / KC;
+        const UnpackConsts magic = unpack_consts();
         ABuf ra;
         BBuf b0, b1;
         load_a(ra, sh, args, 0, rows_active, tid);
@@ -548,7 +595,7 @@ struct Gemm {
                 load_a(ra, sh, args, ch + 1, rows_active, tid);
                 load_b(b1, brow, srow, ch + 1, g);
             }
-            compute_chunk(sh, b0, acc, mt_active, c, g);
+            compute_chunk(sh, b0, acc, mt_active, c, g, magic);
             if (ch + 1 < nchunks) {
                 __syncthreads();
                 store_a(sh, ra, rows_active, tid);
@@ -557,7 +604,7 @@ struct Gemm {
                     load_a(ra, sh, args, ch + 2, rows_active, tid);
                     load_b(b0, brow, srow, ch + 2, g);
                 }
-                compute_chunk(sh, b1, acc, mt_active, c, g);
+                compute_chunk(sh, b1, acc, mt_active, c, g, magic);
             }
         }
 
@@ -589,7 +636,7 @@ struct Gemm {
     }
 
     // SwiGLU on matching gate/up columns; BF16 act rows written in the w2
-    // fragment order together with c2 * (group sum of the rounded values).
+    // fragment order (scaled per frag_shift) with their per-group bias term.
     static __device__ __forceinline__ void epilogue_w13(Shared &sh, const GemmArgs &args,
                                                         const f32x4_t (&acc)[MT][NB], int b,
                                                         int nb, int wave, int c, int g,
@@ -622,12 +669,15 @@ struct Gemm {
             float sum = 0.f;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const uint32_t lo =
-                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, pos0 + 2 * h)];
-                const uint32_t hi =
-                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, pos0 + 2 * h + 1)];
-                sum += bf16_to_f32(lo);
-                sum += bf16_to_f32(hi);
+                const int p0 = pos0 + 2 * h, p1 = p0 + 1;
+                const uint32_t lo = bf16_scaled(
+                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p0)],
+                    frag_shift(bits2, gs2, p0));
+                const uint32_t hi = bf16_scaled(
+                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p1)],
+                    frag_shift(bits2, gs2, p1));
+                sum += bf16_to_f32(lo) * (float)frag_bias_weight(bits2, gs2, p0);
+                sum += bf16_to_f32(hi) * (float)frag_bias_weight(bits2, gs2, p1);
                 o[h] = lo | (hi << 16);
             }
             *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(b * BM + r) * args.N +
@@ -638,13 +688,12 @@ struct Gemm {
         const int gpb = BN / gs2;  // w2 groups per workgroup
         const int per = gs2 / 8;
         const int ngroups2 = args.N / gs2;
-        const float cb = (float)code_bias(bits2);
         for (int q = tid; q < rows_real * gpb; q += NTHREADS) {
             const int r = q / gpb, gl = q % gpb;
             float sum = 0.f;
             for (int k = 0; k < per; ++k)
                 sum += sh.part[r * PIECES + gl * per + k];
-            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * gpb + gl] = cb * sum;
+            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * gpb + gl] = sum;
         }
     }
 };
@@ -687,7 +736,7 @@ struct Stream {
     // dynamic LDS: A rows, their group bias terms, the workgroup's scales
     static __host__ __device__ size_t lds_bytes(int K)
     {
-        return (size_t)R * (K + 8) * 2 + (size_t)R * (K / GS) * 4 +
+        return (size_t)(R + 1) * (K + 8) * 2 + ((size_t)R * (K / GS) + 4) * 4 +
                (size_t)NW * NB * 16 * (K / GS) * 2;
     }
 
@@ -752,28 +801,35 @@ struct Stream {
 
     // MFMAs of one load unit: for each of its groups, the biased-code products
     // start from -c * (row group sum) and are scaled once by the group scale.
+    // All LDS reads of the unit are issued first so their latency overlaps.
     static __device__ __forceinline__ void compute_unit(const uint32_t (&r)[NB][UDW], int u,
                                                         const uint16_t *sA, const float *sBias,
                                                         const uint16_t *sSw, int lds_stride,
                                                         int ngroups, int c, int g,
+                                                        const UnpackConsts &magic,
                                                         f32x4_t (&acc)[NB])
     {
+        bf16x8_t af[GPU][S];
+        f32x4_t negb[GPU];
+        float sc[GPU][NB];
+        const uint16_t *arow = sA + (c < R ? c : R) * lds_stride;
 #pragma unroll
         for (int gq = 0; gq < GPU; ++gq) {
             const int G = u * GPU + gq;
-            f32x4_t negb;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float bv = sBias[v * ngroups + G];  // same address in every lane
-                negb[v] = g == 0 ? -bv : 0.f;
-            }
+            for (int s = 0; s < S; ++s)
+                af[gq][s] = *reinterpret_cast<const bf16x8_t *>(arow + G * GS + (s * 4 + g) * 8);
+            // rows 0..R-1 sit in lane group 0; other lanes read the zero block
+            negb[gq] = *reinterpret_cast<const f32x4_t *>(sBias + (g == 0 ? G * R : ngroups * R));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                sc[gq][j] = f16_to_f32(sSw[(j * 16 + c) * ngroups + G]);
+        }
+#pragma unroll
+        for (int gq = 0; gq < GPU; ++gq) {
             f32x4_t accg[NB];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(
-                    sA + (c < R ? c : 0) * lds_stride + G * GS + (s * 4 + g) * 8);
-                if (c >= R)
-                    af = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     uint32_t cw[4];
@@ -790,20 +846,17 @@ struct Stream {
                         cw[0] = r[j][gq];
                     }
                     constexpr int NDW = CodeTraits<BITS, GS>::NDW;
-                    const bf16x8_t bf =
-                        unpack<BITS, GS, NDW>(reinterpret_cast<const uint32_t(&)[NDW]>(cw), s, g);
-                    accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf,
-                                                                      s == 0 ? negb : accg[j],
-                                                                      0, 0, 0);
+                    const bf16x8_t bf = unpack<BITS, GS, NDW>(
+                        reinterpret_cast<const uint32_t(&)[NDW]>(cw), s, g, magic);
+                    accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af[gq][s], bf, s == 0 ? negb[gq] : accg[j], 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const float sc = f16_to_f32(sSw[(j * 16 + c) * ngroups + G]);
+            for (int j = 0; j < NB; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    acc[j][v] = fmaf(sc, accg[j][v], acc[j][v]);
-            }
+                    acc[j][v] = fmaf(sc[gq][j], accg[j][v], acc[j][v]);
         }
     }
 
@@ -816,10 +869,12 @@ struct Stream {
         const int K = args.K;
         const int ngroups = K / GS;
         const int lds_stride = K + 8;
+        // LDS: R activation rows + a zero row; the rows' negated bias terms as
+        // [group][row] + 4 zeros; the workgroup's scales
         uint16_t *sA = reinterpret_cast<uint16_t *>(smem);
-        float *sBias = reinterpret_cast<float *>(smem + (size_t)R * lds_stride * 2);
-        uint16_t *sS = reinterpret_cast<uint16_t *>(smem + (size_t)R * lds_stride * 2 +
-                                                    (size_t)R * ngroups * 4);
+        float *sBias = reinterpret_cast<float *>(smem + (size_t)(R + 1) * lds_stride * 2);
+        uint16_t *sS = reinterpret_cast<uint16_t *>(smem + (size_t)(R + 1) * lds_stride * 2 +
+                                                    ((size_t)R * ngroups + 4) * 4);
         __shared__ float s_part[R][NW * (W13 ? NB / 2 : 1)];
 
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -852,59 +907,36 @@ struct Stream {
         }
         const int nunits = K / UK;
 
+        // The weight stream starts first: its HBM latency overlaps the staging.
+        uint32_t q[D][NB][UDW];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            load_unit(q[d], brow, d, g);
+
         // Activation rows (zero for padding rows), their bias terms and this
-        // workgroup's scales go to LDS first, in branch-free batches of loads.
+        // workgroup's scales go to LDS.  Each pass issues all of its loads
+        // before its first LDS store, so the latencies overlap.
         {
             const int k8n = K / 8;
-            const int apieces = R * k8n;
-            for (int i0 = 0; i0 < apieces; i0 += 4 * NTHREADS) {
-                u32x4_t v[4];
-                int at[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int i = i0 + t * NTHREADS + tid;
-                    const int ic = i < apieces ? i : apieces - 1;
-                    const int r = ic / k8n, k8 = ic % k8n;
-                    int sr = src[0];
-#pragma unroll
-                    for (int rr = 1; rr < R; ++rr)
-                        sr = r == rr ? src[rr] : sr;
-                    v[t] = *reinterpret_cast<const u32x4_t *>(args.a + (size_t)(sr >= 0 ? sr : 0) * K +
-                                                              k8 * 8);
-                    if (sr < 0)
-                        v[t] = u32x4_t{0u, 0u, 0u, 0u};
-                    at[t] = i < apieces ? r * lds_stride + k8 * 8 : -1;
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (at[t] >= 0)
-                        *reinterpret_cast<u32x4_t *>(sA + at[t]) = v[t];
-            }
-            if (tid < R * ngroups || R * ngroups > NTHREADS) {
-                for (int i = tid; i < R * ngroups; i += NTHREADS) {
-                    const int r = i / ngroups;
-                    int sr = src[0];
-#pragma unroll
-                    for (int rr = 1; rr < R; ++rr)
-                        sr = r == rr ? src[rr] : sr;
-                    const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups + i % ngroups];
-                    sBias[i] = sr >= 0 ? bv : 0.f;
-                }
-            }
-            // scales of the workgroup's 16*NB*NW weight rows: row-contiguous runs
-            // of ngroups halves, copied 8 at a time when the run allows it
             const int srows = NW * NB * 16;
-            if (ngroups % 8 == 0 && reinterpret_cast<uintptr_t>(args.scales) % 16 == 0) {
-                const int per = ngroups / 8;
-                const int spieces = srows * per;
-                for (int i0 = 0; i0 < spieces; i0 += 4 * NTHREADS) {
-                    u32x4_t v[4];
-                    int at[4];
+            const bool svec = ngroups % 8 == 0 && reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
+            const int sper = ngroups / 8;                  // 16-byte scale pieces per row
+            const int spieces = svec ? srows * sper : 0;
+            for (int k0 = 0; k0 < k8n || k0 < spieces; k0 += 2 * NTHREADS) {
+                u32x4_t v[2][R], vs[2];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int i = i0 + t * NTHREADS + tid;
-                        const int ic = i < spieces ? i : spieces - 1;
-                        const int rr = ic / per, k = ic % per;
+                for (int t = 0; t < 2; ++t) {
+                    const int k8 = k0 + t * NTHREADS + tid;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        v[t][r] = u32x4_t{0u, 0u, 0u, 0u};
+                        if (src[r] >= 0 && k8 < k8n)
+                            v[t][r] = reinterpret_cast<const u32x4_t *>(args.a +
+                                                                        (size_t)src[r] * K)[k8];
+                    }
+                    vs[t] = u32x4_t{0u, 0u, 0u, 0u};
+                    if (k8 < spieces) {
+                        const int rr = k8 / sper, kk = k8 % sper;
                         const int w = rr / (NB * 16), j = (rr / 16) % NB, cc = rr % 16;
                         int n;
                         if constexpr (W13)
@@ -912,16 +944,37 @@ struct Stream {
                                 (j >= NB / 2 ? args.N : 0);
                         else
                             n = nb * BN + w * COLS + j * 16 + cc;
-                        v[t] = *reinterpret_cast<const u32x4_t *>(
-                            args.scales + ((size_t)e * nrows + n) * ngroups + k * 8);
-                        at[t] = i < spieces ? rr * ngroups + k * 8 : -1;
+                        vs[t] = *reinterpret_cast<const u32x4_t *>(
+                            args.scales + ((size_t)e * nrows + n) * ngroups + kk * 8);
                     }
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (at[t] >= 0)
-                            *reinterpret_cast<u32x4_t *>(sS + at[t]) = v[t];
                 }
-            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int k8 = k0 + t * NTHREADS + tid;
+                    if (k8 < k8n) {
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            reinterpret_cast<u32x4_t *>(sA + r * lds_stride)[k8] = v[t][r];
+                        reinterpret_cast<u32x4_t *>(sA + R * lds_stride)[k8] =
+                            u32x4_t{0u, 0u, 0u, 0u};
+                    }
+                    if (k8 < spieces)
+                        *reinterpret_cast<u32x4_t *>(sS + (k8 / sper) * ngroups + (k8 % sper) * 8) =
+                            vs[t];
+                }
+            }
+            for (int i = tid; i < R * ngroups + 4; i += NTHREADS) {
+                const int G = i / R, r = i % R;   // [group][row]; the last 4 stay zero
+                int sr = src[0];
+#pragma unroll
+                for (int rr = 1; rr < R; ++rr)
+                    sr = r == rr ? src[rr] : sr;
+                sr = i < R * ngroups ? sr : -1;
+                const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups +
+                                             (G < ngroups ? G : 0)];
+                sBias[i] = sr >= 0 ? -bv : 0.f;  // negated: the start of each MFMA chain
+            }
+            if (!svec) {   // scales without 16-byte alignment: one half at a time
                 for (int i = tid; i < srows * ngroups; i += NTHREADS) {
                     const int rr = i / ngroups, G = i % ngroups;
                     const int w = rr / (NB * 16), j = (rr / 16) % NB, cc = rr % 16;
@@ -936,12 +989,8 @@ struct Stream {
             }
         }
         __syncthreads();
-        // the weight stream: D load units per subtile in flight from here on
-        uint32_t q[D][NB][UDW];
-#pragma unroll
-        for (int d = 0; d < D; ++d)
-            load_unit(q[d], brow, d, g);
 
+        const UnpackConsts magic = unpack_consts();
         f32x4_t acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j)
@@ -949,24 +998,27 @@ struct Stream {
         const uint16_t *sSw = sS + (size_t)wave * NB * 16 * ngroups;
 
         // nunits is a multiple of D (checked by the host): the steady state
-        // reloads every slot unconditionally, the last round only drains.
+        // reloads every slot as soon as its unit is consumed, the last round
+        // only drains.
         int u0 = 0;
         for (; u0 + D < nunits; u0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                uint32_t r[NB][UDW];
-                take_unit(r, q[d]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    regroup(q[d][j]);
+                compute_unit(q[d], u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, magic, acc);
                 load_unit(q[d], brow, u0 + d + D, g);
                 // keep the reload here: moving it later would drain the pipeline
                 __builtin_amdgcn_sched_barrier(0);
-                compute_unit(r, u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, acc);
             }
         }
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            uint32_t r[NB][UDW];
-            take_unit(r, q[d]);
-            compute_unit(r, u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, acc);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                regroup(q[d][j]);
+            compute_unit(q[d], u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, magic, acc);
         }
 
         // rows 0..3 of every subtile live in lane group 0, element v = row
@@ -974,20 +1026,22 @@ struct Stream {
             constexpr int NG = NB / 2;
             const int gs2 = args.gs_next, bits2 = args.bits_next;
             const int ngroups2 = args.N / gs2;
-            const float cb = (float)code_bias(bits2);
 #pragma unroll
             for (int j = 0; j < NG; ++j) {
                 const int n = nb * BN + wave * COLS + j * 16 + c;  // gate column
                 const int G2 = n / gs2;
-                const int pos = G2 * gs2 + frag_dst(bits2, gs2, n % gs2);
+                const int pin = frag_dst(bits2, gs2, n % gs2);
+                const int pos = G2 * gs2 + pin;
+                const int esh = frag_shift(bits2, gs2, pin);
+                const float wgt = (float)frag_bias_weight(bits2, gs2, pin);
 #pragma unroll
                 for (int v = 0; v < R; ++v) {
                     float a = 0.f;
                     if (g == 0 && v < rows_real) {
                         a = swiglu(acc[j][v], acc[NG + j][v], args.alpha, args.beta, args.clamp);
-                        const uint16_t ab = f32_to_bf16(a);
-                        args.act_out[(size_t)(b * R + v) * args.N + pos] = ab;
-                        a = bf16_to_f32(ab);
+                        const uint32_t st = bf16_scaled(f32_to_bf16(a), esh);
+                        args.act_out[(size_t)(b * R + v) * args.N + pos] = (uint16_t)st;
+                        a = bf16_to_f32(st) * wgt;
                     }
                     // sum of the 16 columns of this subtile (lanes 0..15)
 #pragma unroll
@@ -1009,7 +1063,7 @@ struct Stream {
                 for (int t = 0; t < gspan; ++t)
                     sum += s_part[v][k * gspan + t];
                 const int G2 = (nb * BN + k * gspan * 16) / gs2;
-                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, cb * sum);
+                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, sum);
             }
         } else {
             if (g == 0) {
@@ -1030,7 +1084,7 @@ struct Stream {
 };
 
 template <int BITS, int GS, int NB, int D, bool W13>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void stream_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void stream_kernel(
     const GemmArgs args)
 {
     Stream<BITS, GS, NB, D, W13>::run(args);
@@ -1078,7 +1132,8 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
     hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(1 + nprep + (int)nzero),
                           dim3(kAlignThreads), 0, stream, ev.start, ev.stop, 0, x, ids, d.T, d.H,
                           d.topk, d.E, d.block_m, nprep,
-                          (size_t)d.max_tiles * d.block_m * (d.I / d.g2), ws);
+                          (size_t)d.max_tiles * d.block_m * (d.I / d.g2),
+ ws);
     return hipGetLastError();
 }
 
@@ -1106,7 +1161,10 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
 {
     if (variant == 2) {
         constexpr int NB = 2;
-        constexpr int D = Stream<BITS, GS, NB, 4, W13>::SPLIT ? 2 : 4;
+        // load units in flight per wave: as many as fit without spilling
+        constexpr int D = Stream<BITS, GS, NB, 1, W13>::SPLIT      ? 1
+                          : Stream<BITS, GS, NB, 1, W13>::GPU == 4 ? 2
+                                                                   : 4;
         using K_ = Stream<BITS, GS, NB, D, W13>;
         using K1 = Stream<BITS, GS, NB, 1, W13>;
         const dim3 grid(max_tiles, a.N / K_::BN);
@@ -1194,10 +1252,12 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
 
 size_t decode_lds_bytes(int K, int gs)
 {
-    // rows, their bias terms and the scales of 2 subtiles per wave (any bit width)
-    using S_ = Stream<2, 128, 2, 8, true>;
-    return (size_t)S_::R * (K + 8) * 2 + (size_t)S_::R * (K / gs) * 4 +
-           (size_t)S_::NW * 2 * 16 * (K / gs) * 2;
+    // the layout of Stream::lds_bytes, which depends on the group size only
+    switch (gs) {
+    case 32: return Stream<4, 32, 2, 1, true>::lds_bytes(K);
+    case 64: return Stream<4, 64, 2, 1, true>::lds_bytes(K);
+    default: return Stream<4, 128, 2, 1, true>::lds_bytes(K);
+    }
 }
 
 hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,

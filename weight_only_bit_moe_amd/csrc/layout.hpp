@@ -58,8 +58,29 @@ WNA16_HD int frag_dst(int bits, int gs, int off)
     return (s * 4 + g) * 8 + v;
 }
 
-// Bias of the unpacked codes: a stored field u becomes the BF16 value 128 + u,
-// i.e. q + 128 + 2^(bits-1).
-WNA16_HD int code_bias(int bits) { return 128 + (1 << (bits - 1)); }
+// 2-bit fields are turned into BF16 without first shifting them down: the
+// fields of one 32-bit word are read at bit offsets 0, 2 and 4 of the word
+// shifted right by 0, 6 or 12, giving the BF16 number 128 + m*u with
+// m = 1, 4 or 16.  The activation at that fragment position is stored divided
+// by m (an exact power-of-two scaling), so the product is x*(128/m + u).
+// frag_shift returns log2(m) for fragment position pos (0 for 4-bit codes).
+WNA16_HD int frag_shift(int bits, int gs, int pos)
+{
+    if (bits == 4)
+        return 0;
+    const int s = pos >> 5, g = (pos >> 3) & 3, v = pos & 7;
+    const int h = (gs == 32) ? (g & 1) : (s & 1);  // half of the word (fields 4h..4h+3)
+    const int i = 4 * h + (v >> 1);                // field pair (i, i + 8)
+    return 2 * (i % 3);
+}
+
+// With a = x/m and the operand 128 + m*u = 128 + m*(q + 2^(bits-1)):
+//   x*q = a*(128 + m*u) - a*(128 + m*2^(bits-1)).
+// frag_bias_weight is that last factor, so the sum of x*q over a group is the
+// MFMA result minus (sum over the group of a * frag_bias_weight).
+WNA16_HD int frag_bias_weight(int bits, int gs, int pos)
+{
+    return 128 + ((1 << (bits - 1)) << frag_shift(bits, gs, pos));
+}
 
 }  // namespace wna16
