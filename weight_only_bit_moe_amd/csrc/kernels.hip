@@ -266,16 +266,13 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Grouped WNA16 GEMM.
+// Pieces shared by the grouped WNA16 GEMM kernels.
 //
-// Workgroup = NW waves; tile rows BM = 16*MT (pairs of one expert); each wave
-// owns NT column subtiles of 16 (W13: NT gate subtiles and the NT matching up
-// subtiles).  Lane l: column c = l % 16 of each subtile, lane group g = l / 16.
-// Per K group the lane needs gs/4 codes of its row: the contiguous codes
-// [g*gs/4, (g+1)*gs/4) of that group (a 2-bit 32-group: half of dword g/2),
-// i.e. NDW dwords loaded with one 16/8/4-byte load straight into registers.
-// A (activation rows, already in fragment order) goes through LDS in chunks of
-// KC elements; codes and scales of chunk c+1 are loaded while chunk c runs.
+// Lane l of an MFMA works on column c = l % 16 of a 16-column subtile and is
+// in lane group g = l / 16.  Per K group it needs gs/4 codes of its weight
+// row: the contiguous codes [g*gs/4, (g+1)*gs/4) of that group (a 2-bit
+// 32-group: half of dword g/2), i.e. NDW dwords that one 16/8/4-byte load
+// brings straight into registers.
 // ---------------------------------------------------------------------------
 struct GemmArgs {
     const uint16_t *a;        // W13: x_perm [T][K]; W2: act [slots][K]
@@ -390,161 +387,166 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
     return gc / (1.0f + __expf(-alpha * gc)) * (uc + beta);
 }
 
-template <int BITS, int GS, int MT, int NT, int NW, int KC, bool W13>
-struct Gemm {
-    static constexpr int BM = 16 * MT;
-    static constexpr int NB = W13 ? 2 * NT : NT;  // B subtiles per wave
-    static constexpr int BN = NW * NT * 16;       // output columns per workgroup
-    static constexpr int GPC = KC / GS;           // groups per chunk
+// ---------------------------------------------------------------------------
+// Prefill-shaped grouped WNA16 GEMM ("tile" kernel).
+//
+// Workgroup = 4 waves on one tile of up to 64 (token, slot) rows of one
+// expert and 256 weight rows (w13: 128 gate rows and the 128 matching up
+// rows; w2: 256 output columns).  The waves split the weight rows (64 each,
+// four 16-column subtiles), so every wave multiplies all of the tile's row
+// subtiles: each unpacked code fragment feeds up to 4 MFMAs and each
+// activation fragment 4.  Row subtiles beyond the tile's real rows are
+// skipped, so a 5-row expert costs one subtile, not four.
+//
+// K runs in chunks of 128.  Activation rows (already in fragment order) are
+// staged in LDS in "MFMA-ready" order -- [row subtile][step][lane] 16-byte
+// pieces, so every fragment read is one conflict-free ds_read_b128 -- with a
+// double buffer and one barrier per chunk.  Codes and scales go straight from
+// memory into registers, one chunk ahead.
+//
+// Workgroup ids are spread over the 8 XCDs round-robin by the hardware; the
+// kernel gives each XCD a contiguous run of (tile, column block) items,
+// tile-major, so one XCD's L2 serves both the 16 column blocks of a tile
+// (activation reuse) and consecutive tiles of one expert (weight reuse).
+// ---------------------------------------------------------------------------
+template <int BITS, int GS, bool W13>
+struct Tile {
+    static constexpr int BM = 64, MT = 4, NT = 4, NW = 4, NTHREADS = NW * 64;
+    static constexpr int BN = NW * NT * 16;          // weight rows per workgroup
+    static constexpr int OUTC = W13 ? BN / 2 : BN;   // output columns per workgroup
+    static constexpr int KC = 128;                   // K per chunk
+    static constexpr int GPC = KC / GS;              // groups per chunk
+    static constexpr int S = GS / 32;                // MFMA steps per group
     static constexpr int NDW = CodeTraits<BITS, GS>::NDW;
-    static constexpr int S = CodeTraits<BITS, GS>::S;
-    static constexpr int LDS_STRIDE = KC + 8;     // bf16 elements; rows 16 B apart mod 256 B
-    static constexpr int NTHREADS = NW * 64;
+    static constexpr int ACT_STRIDE = OUTC + 8;      // W13 epilogue tile, bf16 elements
+    static constexpr int kXcds = 8;
 
+    struct EpiW13 {
+        uint16_t act[BM * ACT_STRIDE];
+        float part[BM * (OUTC / 8)];
+    };
     struct Shared {
-        uint16_t a[BM * LDS_STRIDE];
-        float bias[BM * GPC];
-        float part[BM * (BN / 8)];
-        int row_src[BM];
+        union {
+            u32x4_t a[2][MT * 4 * 64];   // [buffer][subtile][step][lane]
+            EpiW13 epi;
+        };
+        float nbias[2][MT * GPC * 16];   // [buffer][subtile][group][row]: -(bias term)
         int row_pair[BM];
+        int row_src[BM];
         int rows_real;
     };
 
-    struct BBuf {
-        uint32_t q[NB][GPC][NDW];
-        float s[NB][GPC];
+    struct AStage {
+        u32x4_t v[MT];
+        float nb;
+    };
+    struct BStage {
+        uint32_t q[NT][GPC][NDW];
+        uint16_t s[NT][GPC];
     };
 
-    static __device__ __forceinline__ void load_b(BBuf &buf, const uint32_t *const *brow,
-                                                  const uint16_t *const *srow, int chunk, int g)
+    static __device__ __forceinline__ void load_a(AStage &st, const uint16_t *const (&arow)[MT],
+                                                  const float *brow, int kc, int mt_active,
+                                                  int tid)
+    {
+        const int koff = kc * KC + (tid >> 6) * 32 + ((tid >> 4) & 3) * 8;
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            if (j < mt_active)
+                st.v[j] = *reinterpret_cast<const u32x4_t *>(arow[j] + koff);
+        if (tid < mt_active * GPC * 16)
+            st.nb = -brow[kc * GPC + (tid >> 4) % GPC];
+    }
+
+    static __device__ __forceinline__ void store_a(Shared &sh, int buf, const AStage &st,
+                                                   int mt_active, int tid)
     {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < MT; ++j)
+            if (j < mt_active)
+                sh.a[buf][j * 256 + tid] = st.v[j];
+        if (tid < mt_active * GPC * 16)
+            sh.nbias[buf][tid] = st.nb;
+    }
+
+    static __device__ __forceinline__ void load_b(BStage &st, const uint32_t *const (&crow)[NT],
+                                                  const uint16_t *const (&srow)[NT], int kc, int g)
+    {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int G = 0; G < GPC; ++G) {
-                const int Gg = chunk * GPC + G;
-                load_codes<NDW>(buf.q[j][G], brow[j] + CodeTraits<BITS, GS>::dword_off(Gg, g));
-                buf.s[j][G] = f16_to_f32(srow[j][Gg]);
+                const int Gg = kc * GPC + G;
+                load_codes<NDW>(st.q[j][G], crow[j] + CodeTraits<BITS, GS>::dword_off(Gg, g));
+                st.s[j][G] = srow[j][Gg];
             }
-        }
     }
 
-    // A chunk held in registers between its global load and its LDS store.
-    static constexpr int PIECES = KC / 8;  // 16-byte pieces per row and chunk
-    static constexpr int MAXP = (BM * PIECES + NTHREADS - 1) / NTHREADS;
-    static constexpr int MAXB = (BM * GPC + NTHREADS - 1) / NTHREADS;
-    struct ABuf {
-        u32x4_t v[MAXP];
-        float bias[MAXB];
-    };
-
-    static __device__ __forceinline__ void load_a(ABuf &ra, const Shared &sh, const GemmArgs &args,
-                                                  int chunk, int rows_active, int tid)
-    {
-        const int ngroups = args.K / GS;
-#pragma unroll
-        for (int k = 0; k < MAXP; ++k) {
-            const int q = tid + k * NTHREADS;
-            ra.v[k] = u32x4_t{0u, 0u, 0u, 0u};
-            if (q < rows_active * PIECES) {
-                const int src = sh.row_src[q / PIECES];
-                if (src >= 0)
-                    ra.v[k] = *reinterpret_cast<const u32x4_t *>(
-                        args.a + (size_t)src * args.K + (size_t)chunk * KC + (q % PIECES) * 8);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < MAXB; ++k) {
-            const int q = tid + k * NTHREADS;
-            ra.bias[k] = 0.f;
-            if (q < rows_active * GPC) {
-                const int src = sh.row_src[q / GPC];
-                if (src >= 0)
-                    ra.bias[k] = args.a_bias[(size_t)src * ngroups + chunk * GPC + q % GPC];
-            }
-        }
-    }
-
-    static __device__ __forceinline__ void store_a(Shared &sh, const ABuf &ra, int rows_active,
-                                                   int tid)
-    {
-#pragma unroll
-        for (int k = 0; k < MAXP; ++k) {
-            const int q = tid + k * NTHREADS;
-            if (q < rows_active * PIECES)
-                *reinterpret_cast<u32x4_t *>(&sh.a[(q / PIECES) * LDS_STRIDE + (q % PIECES) * 8]) =
-                    ra.v[k];
-        }
-#pragma unroll
-        for (int k = 0; k < MAXB; ++k) {
-            const int q = tid + k * NTHREADS;
-            if (q < rows_active * GPC)
-                sh.bias[q] = ra.bias[k];
-        }
-    }
-
-    static __device__ __forceinline__ void compute_chunk(const Shared &sh, const BBuf &buf,
-                                                         f32x4_t (&acc)[MT][NB], int mt_active,
-                                                         int c, int g, const UnpackConsts &magic)
+    static __device__ __forceinline__ void compute(const Shared &sh, int buf, const BStage &bs,
+                                                   f32x4_t (&acc)[MT][NT], int mt_active,
+                                                   int lane, int g, const UnpackConsts &magic)
     {
 #pragma unroll
         for (int G = 0; G < GPC; ++G) {
-            f32x4_t negb[MT];
+            bf16x8_t bf[NT][S];
+            float sc[NT];
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
+            for (int j = 0; j < NT; ++j) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    negb[i][v] = -sh.bias[(16 * i + 4 * g + v) * GPC + G];
-            f32x4_t accg[MT][NB];
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                bf16x8_t af[MT];
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    if (i < mt_active)
-                        af[i] = *reinterpret_cast<const bf16x8_t *>(
-                            &sh.a[(16 * i + c) * LDS_STRIDE + G * GS + (s * 4 + g) * 8]);
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const bf16x8_t bf = unpack<BITS, GS, NDW>(buf.q[j][G], s, g, magic);
-#pragma unroll
-                    for (int i = 0; i < MT; ++i)
-                        if (i < mt_active)
-                            accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                af[i], bf, s == 0 ? negb[i] : accg[i][j], 0, 0, 0);
-                }
+                for (int s = 0; s < S; ++s)
+                    bf[j][s] = unpack<BITS, GS, NDW>(bs.q[j][G], s, g, magic);
+                sc[j] = f16_to_f32(bs.s[j][G]);
             }
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-                if (i < mt_active)
+            for (int i = 0; i < MT; ++i) {
+                if (i >= mt_active)
+                    continue;
+                bf16x8_t af[S];
 #pragma unroll
-                    for (int j = 0; j < NB; ++j)
+                for (int s = 0; s < S; ++s)
+                    af[s] = __builtin_bit_cast(bf16x8_t, sh.a[buf][(i * 4 + G * S + s) * 64 + lane]);
+                const f32x4_t nb =
+                    *reinterpret_cast<const f32x4_t *>(&sh.nbias[buf][(i * GPC + G) * 16 + 4 * g]);
+                f32x4_t accg[NT];
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[i][j][v] = fmaf(buf.s[j][G], accg[i][j][v], acc[i][j][v]);
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            af[s], bf[j][s], s == 0 ? nb : accg[j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[i][j][v] = fmaf(sc[j], accg[j][v], acc[i][j][v]);
+            }
         }
     }
 
     static __device__ void run(const GemmArgs &args)
     {
         __shared__ __align__(16) Shared sh;
-        const int b = blockIdx.x;
-        if (b >= *args.num_tiles)
-            return;
-        const int nb = blockIdx.y;
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int c = lane & 15, g = lane >> 4;
+
+        // (tile, column block) item of this workgroup
+        const int nblk = (args.N + OUTC - 1) / OUTC;
+        const int total = *args.num_tiles * nblk;
+        const int per = (total + kXcds - 1) / kXcds;
+        const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+        const int item = xcd * per + j;
+        if (j >= per || item >= total)
+            return;
+        const int b = item / nblk, nb = item % nblk;
         const int e = args.tile_expert[b];
 
         if (tid < 64) {
-            int p = args.P;
-            if (tid < BM)
-                p = args.sorted_ids[b * BM + tid];
-            const bool real = tid < BM && p < args.P;
-            if (tid < BM) {
-                sh.row_pair[tid] = p;
-                sh.row_src[tid] = real ? (W13 ? p / args.topk : b * BM + tid) : -1;
-            }
+            const int p = args.sorted_ids[b * BM + tid];
+            const bool real = p < args.P;
+            const int src0 = W13 ? args.sorted_ids[b * BM] / args.topk : b * BM;
+            sh.row_pair[tid] = p;
+            // padding rows read row 0's data: their results are never stored
+            sh.row_src[tid] = real ? (W13 ? p / args.topk : b * BM + tid) : src0;
             const uint64_t m = __ballot(real);
             if (tid == 0)
                 sh.rows_real = __popcll(m);
@@ -552,69 +554,85 @@ struct Gemm {
         __syncthreads();
         const int rows_real = sh.rows_real;
         const int mt_active = (rows_real + 15) >> 4;
-        const int rows_active = mt_active * 16;
+        const int K = args.K;
+        const int ngroups = K / GS;
 
-        // this lane's B rows
-        const int nrows = W13 ? 2 * args.N : args.N;
-        const int kw = args.K * BITS / 32;
-        const int ngroups = args.K / GS;
-        const uint32_t *brow[NB];
-        const uint16_t *srow[NB];
+        // activation rows this thread stages, and the bias row
+        const uint16_t *arow[MT];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int jj = W13 ? (j % NT) : j;
-            int n = nb * BN + wave * NT * 16 + jj * 16 + c;
-            if (W13 && j >= NT)
-                n += args.N;  // up projection rows follow the gate rows
+        for (int i = 0; i < MT; ++i)
+            arow[i] = args.a + (size_t)sh.row_src[i * 16 + (tid & 15)] * K;
+        const int brow_r = (tid / (GPC * 16)) * 16 + (tid & 15);
+        const float *brow = args.a_bias + (size_t)sh.row_src[brow_r < BM ? brow_r : 0] * ngroups;
+
+        // this lane's weight rows (a wave past the last column stays idle but
+        // keeps taking part in the staging and the barriers)
+        const int nrows = W13 ? 2 * args.N : args.N;
+        const int col0 = nb * OUTC + wave * (W13 ? NT / 2 : NT) * 16;
+        const bool wave_on = col0 < args.N;
+        const int kw = K * BITS / 32;
+        const uint32_t *crow[NT];
+        const uint16_t *srow[NT];
+#pragma unroll
+        for (int jj = 0; jj < NT; ++jj) {
+            int n;
+            if constexpr (W13)
+                n = col0 + (jj % (NT / 2)) * 16 + c + (jj >= NT / 2 ? args.N : 0);
+            else
+                n = col0 + jj * 16 + c;
+            n = wave_on ? n : 0;
             const size_t row = (size_t)e * nrows + n;
-            brow[j] = args.codes + row * kw;
-            srow[j] = args.scales + row * ngroups;
+            crow[jj] = args.codes + row * kw;
+            srow[jj] = args.scales + row * ngroups;
         }
 
-        f32x4_t acc[MT][NB];
+        f32x4_t acc[MT][NT];
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < NT; ++jj)
+                acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Software pipeline: chunk ch+1's activation and weight loads are in
-        // flight while chunk ch runs on the MFMAs.  Activation loads are issued
-        // before weight loads so that waiting for them never waits for HBM.
-        const int nchunks = args.K / KC;
         const UnpackConsts magic = unpack_consts();
-        ABuf ra;
-        BBuf b0, b1;
-        load_a(ra, sh, args, 0, rows_active, tid);
-        load_b(b0, brow, srow, 0, g);
-        for (int ch = 0; ch < nchunks; ch += 2) {
-            __syncthreads();
-            store_a(sh, ra, rows_active, tid);
-            __syncthreads();
-            if (ch + 1 < nchunks) {
-                load_a(ra, sh, args, ch + 1, rows_active, tid);
-                load_b(b1, brow, srow, ch + 1, g);
+        const int nchunks = K / KC;
+        const int mt_w = wave_on ? mt_active : 0;   // subtiles this wave multiplies
+        AStage as;
+        BStage b0, b1;
+        load_a(as, arow, brow, 0, mt_active, tid);
+        if (wave_on)
+            load_b(b0, crow, srow, 0, g);
+        store_a(sh, 0, as, mt_active, tid);
+        __syncthreads();
+        for (int kc = 0; kc < nchunks; kc += 2) {
+            if (kc + 1 < nchunks) {
+                load_a(as, arow, brow, kc + 1, mt_active, tid);
+                if (wave_on)
+                    load_b(b1, crow, srow, kc + 1, g);
             }
-            compute_chunk(sh, b0, acc, mt_active, c, g, magic);
-            if (ch + 1 < nchunks) {
-                __syncthreads();
-                store_a(sh, ra, rows_active, tid);
-                __syncthreads();
-                if (ch + 2 < nchunks) {
-                    load_a(ra, sh, args, ch + 2, rows_active, tid);
-                    load_b(b0, brow, srow, ch + 2, g);
+            compute(sh, 0, b0, acc, mt_w, lane, g, magic);
+            if (kc + 1 < nchunks)
+                store_a(sh, 1, as, mt_active, tid);
+            __syncthreads();
+            if (kc + 1 < nchunks) {
+                if (kc + 2 < nchunks) {
+                    load_a(as, arow, brow, kc + 2, mt_active, tid);
+                    if (wave_on)
+                        load_b(b0, crow, srow, kc + 2, g);
                 }
-                compute_chunk(sh, b1, acc, mt_active, c, g, magic);
+                compute(sh, 1, b1, acc, mt_w, lane, g, magic);
+                if (kc + 2 < nchunks)
+                    store_a(sh, 0, as, mt_active, tid);
+                __syncthreads();
             }
         }
 
         if constexpr (W13) {
-            epilogue_w13(sh, args, acc, b, nb, wave, c, g, rows_real, mt_active, tid);
+            epilogue_w13(sh, args, acc, b, nb, wave, c, g, rows_real, mt_w, tid);
         } else {
             // routing-weighted scatter-add into the FP32 accumulator
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                if (i >= mt_active)
+                if (i >= mt_w)
                     continue;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -622,48 +640,47 @@ struct Gemm {
                     if (r >= rows_real)
                         continue;
                     const int p = sh.row_pair[r];
-                    const int t = p / args.topk;
                     const float w = args.topk_w[p];
-                    float *orow = args.out_f32 + (size_t)t * args.N;
+                    float *orow = args.out_f32 + (size_t)(p / args.topk) * args.N + col0 + c;
 #pragma unroll
-                    for (int j = 0; j < NB; ++j) {
-                        const int n = nb * BN + wave * NT * 16 + j * 16 + c;
-                        unsafeAtomicAdd(orow + n, w * acc[i][j][v]);
-                    }
+                    for (int jj = 0; jj < NT; ++jj)
+                        unsafeAtomicAdd(orow + jj * 16, w * acc[i][jj][v]);
                 }
             }
         }
     }
 
     // SwiGLU on matching gate/up columns; BF16 act rows written in the w2
-    // fragment order (scaled per frag_shift) with their per-group bias term.
+    // fragment order (scaled per frag_shift), with the per-group bias term of
+    // each (row, w2 group): the workgroup covers whole w2 groups (gs2 <= 128).
     static __device__ __forceinline__ void epilogue_w13(Shared &sh, const GemmArgs &args,
-                                                        const f32x4_t (&acc)[MT][NB], int b,
+                                                        const f32x4_t (&acc)[MT][NT], int b,
                                                         int nb, int wave, int c, int g,
-                                                        int rows_real, int mt_active, int tid)
+                                                        int rows_real, int mt_w, int tid)
     {
-        static_assert(BN <= KC, "act tile reuses the A staging buffer");
-        constexpr int ACT_STRIDE = LDS_STRIDE;
-        __syncthreads();  // all waves are done with the last A chunk
+        constexpr int NG = NT / 2;
+        // the union's act tile overlays the A buffers: the loop's last barrier
+        // has already been passed by every wave
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            if (i >= mt_active)
+            if (i >= mt_w)
                 continue;
 #pragma unroll
-            for (int j = 0; j < NT; ++j)
+            for (int jj = 0; jj < NG; ++jj)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float a =
-                        swiglu(acc[i][j][v], acc[i][NT + j][v], args.alpha, args.beta, args.clamp);
-                    sh.a[(16 * i + 4 * g + v) * ACT_STRIDE + wave * NT * 16 + j * 16 + c] =
+                    const float a = swiglu(acc[i][jj][v], acc[i][NG + jj][v], args.alpha,
+                                           args.beta, args.clamp);
+                    sh.epi.act[(16 * i + 4 * g + v) * ACT_STRIDE + wave * NG * 16 + jj * 16 + c] =
                         f32_to_bf16(a);
                 }
         }
         __syncthreads();
         const int gs2 = args.gs_next, bits2 = args.bits_next;
-        constexpr int PIECES = BN / 8;
-        for (int q = tid; q < rows_real * PIECES; q += NTHREADS) {
-            const int r = q / PIECES, c8 = q % PIECES;
+        const int ncols = min(OUTC, args.N - nb * OUTC);
+        const int pieces = ncols / 8;
+        for (int q = tid; q < rows_real * pieces; q += NTHREADS) {
+            const int r = q / pieces, c8 = q % pieces;
             const int gl = (c8 * 8) / gs2, pos0 = (c8 * 8) % gs2;
             u32x4_t o;
             float sum = 0.f;
@@ -671,37 +688,38 @@ struct Gemm {
             for (int h = 0; h < 4; ++h) {
                 const int p0 = pos0 + 2 * h, p1 = p0 + 1;
                 const uint32_t lo = bf16_scaled(
-                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p0)],
+                    sh.epi.act[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p0)],
                     frag_shift(bits2, gs2, p0));
                 const uint32_t hi = bf16_scaled(
-                    sh.a[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p1)],
+                    sh.epi.act[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p1)],
                     frag_shift(bits2, gs2, p1));
                 sum += bf16_to_f32(lo) * (float)frag_bias_weight(bits2, gs2, p0);
                 sum += bf16_to_f32(hi) * (float)frag_bias_weight(bits2, gs2, p1);
                 o[h] = lo | (hi << 16);
             }
             *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(b * BM + r) * args.N +
-                                         nb * BN + c8 * 8) = o;
-            sh.part[r * PIECES + c8] = sum;
+                                         nb * OUTC + c8 * 8) = o;
+            sh.epi.part[r * (OUTC / 8) + c8] = sum;
         }
         __syncthreads();
-        const int gpb = BN / gs2;  // w2 groups per workgroup
+        const int gpb = ncols / gs2;  // w2 groups in this workgroup
         const int per = gs2 / 8;
         const int ngroups2 = args.N / gs2;
         for (int q = tid; q < rows_real * gpb; q += NTHREADS) {
             const int r = q / gpb, gl = q % gpb;
             float sum = 0.f;
             for (int k = 0; k < per; ++k)
-                sum += sh.part[r * PIECES + gl * per + k];
-            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * gpb + gl] = sum;
+                sum += sh.epi.part[r * (OUTC / 8) + gl * per + k];
+            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * (OUTC / gs2) + gl] = sum;
         }
     }
 };
 
-template <int BITS, int GS, int MT, int NT, int NW, int KC, bool W13>
-__global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs args)
+template <int BITS, int GS, bool W13>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tile_kernel(
+    const GemmArgs args)
 {
-    Gemm<BITS, GS, MT, NT, NW, KC, W13>::run(args);
+    Tile<BITS, GS, W13>::run(args);
 }
 
 // ---------------------------------------------------------------------------
@@ -1132,8 +1150,9 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
     hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(1 + nprep + (int)nzero),
                           dim3(kAlignThreads), 0, stream, ev.start, ev.stop, 0, x, ids, d.T, d.H,
                           d.topk, d.E, d.block_m, nprep,
-                          (size_t)d.max_tiles * d.block_m * (d.I / d.g2),
- ws);
+                          // only the decode-shaped w13 adds into act_bias
+                          d.variant13 == 2 ? (size_t)d.max_tiles * d.block_m * (d.I / d.g2) : 0,
+                          ws);
     return hipGetLastError();
 }
 
@@ -1153,8 +1172,8 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
 }
 
 // Tile shapes.  Variant 2 (few rows per expert, HBM-bound): the stream kernel
-// on 4-row tiles.  Variant 1 (many rows per expert, MFMA-bound): 64-row tiles,
-// 4 waves of 2 subtiles per projection half.
+// on 4-row tiles.  Variant 1 (many rows per expert, MFMA-bound): the tile
+// kernel on 64-row tiles.
 template <int BITS, int GS, bool W13>
 static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, hipStream_t stream,
                                 const KernelEvents &ev)
@@ -1177,14 +1196,11 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
                                   dim3(K1::NTHREADS), (uint32_t)K1::lds_bytes(a.K), stream,
                                   ev.start, ev.stop, 0, a);
     } else {
-        constexpr int NW = 4, MT = 4, NT = 2, BN = NW * NT * 16;
-        const dim3 grid(max_tiles, a.N / BN);
-        if (a.K % 256 == 0)
-            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 256, W13>), grid,
-                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
-        else
-            hipExtLaunchKernelGGL((gemm_kernel<BITS, GS, MT, NT, NW, 128, W13>), grid,
-                                  dim3(NW * 64), 0, stream, ev.start, ev.stop, 0, a);
+        using K_ = Tile<BITS, GS, W13>;
+        const long items = (long)max_tiles * ((a.N + K_::OUTC - 1) / K_::OUTC);
+        const long grid = (items + K_::kXcds - 1) / K_::kXcds * K_::kXcds;
+        hipExtLaunchKernelGGL((tile_kernel<BITS, GS, W13>), dim3((unsigned)grid),
+                              dim3(K_::NTHREADS), 0, stream, ev.start, ev.stop, 0, a);
     }
     return hipGetLastError();
 }
