@@ -107,6 +107,8 @@ int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
  *
  * Shapes: T >= 0 (T = 0 returns OK with no launch), 1 <= E <= 1024,
  * 1 <= topk <= 64, H and I multiples of 128, each group dividing its K.
+ * Size limit (EUNSUPPORTED): T*H*2, (T*topk + 64*min(E, T*topk) + 64)*I*2 and
+ * 2*I*H must each stay below 2^32 (the kernels use 32-bit byte offsets).
  * alpha, beta must be finite; clamp must be > 0 (or +INFINITY), not NaN.
  * The output is the FP32 sum rounded to BF16 (nearest even).  Summation
  * order across a token's experts is unspecified (FP32 atomics).

@@ -84,6 +84,8 @@ def call(ptrs=16, ws_bytes=1 << 30, ws_ptr=4096, **over):
     (dict(q13=(3, 128)), Bd.EUNSUPPORTED), (dict(q2=(4, 96)), Bd.EUNSUPPORTED),
     (dict(H=200), Bd.EUNSUPPORTED), (dict(I=64), Bd.EUNSUPPORTED), (dict(E=1025), Bd.EUNSUPPORTED),
     (dict(topk=65), Bd.EUNSUPPORTED), (dict(I=128, q2=(2, 128)), None),
+    (dict(T=1 << 20, H=2048, topk=1), Bd.EUNSUPPORTED),     # T*H*2 = 2^32
+    (dict(T=1 << 17, H=256, I=2048, topk=8), Bd.EUNSUPPORTED),  # act slots * I * 2 > 2^32
 ])
 def test_forward_rejects_before_device(lib, over, status):
     st = call(**over)

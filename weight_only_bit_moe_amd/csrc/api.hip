@@ -97,6 +97,17 @@ void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
     plan->w2_variant = decode ? 2 : 1;
 }
 
+// The prefill-shaped kernels address activations, their bias terms and one
+// expert's codes and scales with 32-bit byte offsets.
+bool offsets_fit(int T, int H, int I, int E, int topk)
+{
+    const unsigned long long lim = 1ull << 32;
+    const unsigned long long P = (unsigned long long)T * topk;
+    const unsigned long long slots = P + 64ull * (unsigned long long)(E < (long long)P ? E : P) + 64;
+    return (unsigned long long)T * H * 2 < lim && slots * I * 2 < lim &&
+           2ull * I * H < lim;   // one expert's w13 codes at 4 bits, and its scales
+}
+
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_arch_ok[64];
 
@@ -190,6 +201,8 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     if (!std::isfinite(alpha) || !std::isfinite(beta) || std::isnan(clamp) || !(clamp > 0.f))
         return MOE_WNA16_EINVAL;
     if (!valid_qparams(q13) || !valid_qparams(q2) || H % q13.group || I % q2.group)
+        return MOE_WNA16_EUNSUPPORTED;
+    if (!offsets_fit(T, H, I, E, topk))
         return MOE_WNA16_EUNSUPPORTED;
     if (T == 0)
         return MOE_WNA16_OK;

@@ -398,17 +398,54 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
 // activation fragment 4.  Row subtiles beyond the tile's real rows are
 // skipped, so a 5-row expert costs one subtile, not four.
 //
-// K runs in chunks of 128.  Activation rows (already in fragment order) are
-// staged in LDS in "MFMA-ready" order -- [row subtile][step][lane] 16-byte
-// pieces, so every fragment read is one conflict-free ds_read_b128 -- with a
-// double buffer and one barrier per chunk.  Codes and scales go straight from
-// memory into registers, one chunk ahead.
+// K runs in chunks of 128.  Every operand of a chunk -- activation rows
+// (already in fragment order), their bias terms, codes and scales -- is
+// copied from memory straight into LDS (global_load_lds, no registers) in
+// the order the MFMA lanes read it, so each read is one conflict-free
+// ds_read.  The copies run 1-2 chunks ahead through a ring of LDS stages,
+// with one barrier per chunk and explicit vmcnt waits.
 //
 // Workgroup ids are spread over the 8 XCDs round-robin by the hardware; the
 // kernel gives each XCD a contiguous run of (tile, column block) items,
 // tile-major, so one XCD's L2 serves both the 16 column blocks of a tile
 // (activation reuse) and consecutive tiles of one expert (weight reuse).
 // ---------------------------------------------------------------------------
+// LDS address (byte offset in the workgroup's LDS) of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
+}
+
+// Copies from global memory straight into LDS (gfx950 global_load_lds):
+// lane l's `bytes` bytes at base + voff land at LDS address lds + l * 16
+// (16-byte copies) or lds + l * 4 (4- and 2-byte copies: every lane writes a
+// whole dword slot; a 2-byte value sits in the slot's low half).
+// `base` and `lds` are wave-uniform.  Written as inline asm so that the
+// compiler does not track them: it would otherwise make every later LDS read
+// wait for all copies in flight, which defeats the multi-stage ring.  The
+// caller waits for them with vmcnt.  (M0 is set here; nothing else in these
+// kernels keeps a value in M0.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void *base, uint32_t voff, uint32_t lds_in)
+{
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+                     "s"(lds)
+                     : "memory", "m0");
+    else if constexpr (BYTES == 4)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base),
+                     "s"(lds)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(base),
+                     "s"(lds)
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int BITS, int GS, bool W13>
 struct Tile {
     static constexpr int BM = 64, MT = 4, NT = 4, NW = 4, NTHREADS = NW * 64;
@@ -418,102 +455,162 @@ struct Tile {
     static constexpr int GPC = KC / GS;              // groups per chunk
     static constexpr int S = GS / 32;                // MFMA steps per group
     static constexpr int NDW = CodeTraits<BITS, GS>::NDW;
+    static constexpr int NDWI = NDW == 4 ? 1 : NDW;  // code copies per (subtile, group)
     static constexpr int ACT_STRIDE = OUTC + 8;      // W13 epilogue tile, bf16 elements
     static constexpr int kXcds = 8;
+
+    // One pipeline stage in LDS, every piece in the order the MFMA lanes read it:
+    //   A      [subtile][step][lane] 16 bytes           16 KB
+    //   bias   [subtile][group][row] floats (negated)    1 KB
+    //   codes  [wave][subtile][group][copy][lane] NDW/NDWI dwords
+    //   scales [wave][group][column][subtile] dword slots (value in the low half)
+    static constexpr int A_OFF = 0;
+    static constexpr int BIAS_OFF = A_OFF + MT * 4 * 64 * 16;
+    static constexpr int B_WAVE = NT * GPC * 64 * NDW * 4;
+    static constexpr int B_OFF = BIAS_OFF + 256 * 4;
+    static constexpr int SC_WAVE = GPC * 64 * 4;
+    static constexpr int SC_OFF = B_OFF + NW * B_WAVE;
+    static constexpr int STAGE = SC_OFF + NW * SC_WAVE;
+    // deepest ring that leaves room for two workgroups per CU
+    static constexpr int STAGES = 3 * STAGE + 1024 <= 80 * 1024 ? 3 : 2;
 
     struct EpiW13 {
         uint16_t act[BM * ACT_STRIDE];
         float part[BM * (OUTC / 8)];
     };
-    struct Shared {
-        union {
-            u32x4_t a[2][MT * 4 * 64];   // [buffer][subtile][step][lane]
-            EpiW13 epi;
-        };
-        float nbias[2][MT * GPC * 16];   // [buffer][subtile][group][row]: -(bias term)
-        int row_pair[BM];
-        int row_src[BM];
-        int rows_real;
+    static_assert(sizeof(EpiW13) <= STAGES * STAGE, "epilogue tile overlays the ring");
+    struct Rows {
+        int pair[BM];
+        int src[BM];
+        int real;
     };
 
-    struct AStage {
-        u32x4_t v[MT];
-        float nb;
-    };
-    struct BStage {
-        uint32_t q[NT][GPC][NDW];
-        uint16_t s[NT][GPC];
+    // Per-lane copy sources: 32-bit byte offsets from workgroup-uniform
+    // bases.  Padding rows and idle waves point at valid rows.
+    struct Ctx {
+        const uint16_t *a;
+        const float *bias;
+        const uint32_t *codes;      // this expert's codes
+        const uint16_t *scales;     // this expert's scales
+        uint32_t aoff[MT];          // activation row of subtile i this lane copies
+        uint32_t boff;              // bias row this lane copies
+        uint32_t coff[NT];          // this lane's weight row in subtile j
+        uint32_t soff;              // weight row whose scales this lane copies
+        uint32_t ring;              // LDS address of the ring
+        int b, nb, col0, tid, lane, wave, g;
+        bool wave_on;
     };
 
-    static __device__ __forceinline__ void load_a(AStage &st, const uint16_t *const (&arow)[MT],
-                                                  const float *brow, int kc, int mt_active,
-                                                  int tid)
+    // Barrier with no memory fence, so the copies of later chunks stay in
+    // flight.  This wave's LDS reads are complete before it (lgkmcnt(0)), and
+    // the asm's memory clobber keeps the compiler from moving LDS accesses
+    // across it.
+    static __device__ __forceinline__ void workgroup_barrier()
     {
-        const int koff = kc * KC + (tid >> 6) * 32 + ((tid >> 4) & 3) * 8;
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-            if (j < mt_active)
-                st.v[j] = *reinterpret_cast<const u32x4_t *>(arow[j] + koff);
-        if (tid < mt_active * GPC * 16)
-            st.nb = -brow[kc * GPC + (tid >> 4) % GPC];
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
-    static __device__ __forceinline__ void store_a(Shared &sh, int buf, const AStage &st,
-                                                   int mt_active, int tid)
+    // vmcnt(n) alone (expcnt and lgkmcnt left at their maximum)
+    template <int N>
+    static __device__ __forceinline__ void wait_vm()
     {
-#pragma unroll
-        for (int j = 0; j < MT; ++j)
-            if (j < mt_active)
-                sh.a[buf][j * 256 + tid] = st.v[j];
-        if (tid < mt_active * GPC * 16)
-            sh.nbias[buf][tid] = st.nb;
+        static_assert(N >= 0 && N < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     }
 
-    static __device__ __forceinline__ void load_b(BStage &st, const uint32_t *const (&crow)[NT],
-                                                  const uint16_t *const (&srow)[NT], int kc, int g)
+    // number of copies each wave issues per chunk
+    template <int MTA>
+    static constexpr int copies() { return MTA + 1 + NT * GPC * NDWI + GPC; }
+
+    // Issue every copy of chunk kc into LDS stage `st` (wave-uniform pointers;
+    // lane l's data lands at ptr + l * size).
+    template <int MTA>
+    static __device__ __forceinline__ void issue(int stage, const Ctx &cx, int kc)
     {
+        const int l = cx.lane;
+        const uint32_t st = cx.ring + stage * STAGE;
+        // activations: this wave copies step `wave` of every active subtile
+        const uint32_t koff = (uint32_t)(kc * KC + cx.wave * 32 + (l >> 4) * 8) * 2u;
+#pragma unroll
+        for (int i = 0; i < MTA; ++i)
+            copy_to_lds<16>(cx.a, cx.aoff[i] + koff, st + A_OFF + (i * 4 + cx.wave) * 64 * 16);
+        // bias terms: entries [64 * wave, 64 * wave + 64) of [subtile][group][row]
+        copy_to_lds<4>(cx.bias,
+                       cx.boff + (uint32_t)(kc * GPC + ((cx.wave * 64 + l) >> 4) % GPC) * 4u,
+                       st + BIAS_OFF + cx.wave * 256);
+        // codes of this wave's weight rows
+        const uint32_t bw = st + B_OFF + cx.wave * B_WAVE;
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int G = 0; G < GPC; ++G) {
-                const int Gg = kc * GPC + G;
-                load_codes<NDW>(st.q[j][G], crow[j] + CodeTraits<BITS, GS>::dword_off(Gg, g));
-                st.s[j][G] = srow[j][Gg];
+                const uint32_t src =
+                    cx.coff[j] + (uint32_t)CodeTraits<BITS, GS>::dword_off(kc * GPC + G, cx.g) * 4u;
+                const uint32_t dst = bw + (j * GPC + G) * 64 * NDW * 4;
+                if constexpr (NDW == 4) {
+                    copy_to_lds<16>(cx.codes, src, dst);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NDWI; ++h)
+                        copy_to_lds<4>(cx.codes, src + h * 4, dst + h * 256);
+                }
             }
+        // scales: lane l copies column l / 4 of subtile l % 4
+        const uint32_t sw = st + SC_OFF + cx.wave * SC_WAVE;
+#pragma unroll
+        for (int G = 0; G < GPC; ++G)
+            copy_to_lds<2>(cx.scales, cx.soff + (uint32_t)(kc * GPC + G) * 2u, sw + G * 256);
     }
 
-    static __device__ __forceinline__ void compute(const Shared &sh, int buf, const BStage &bs,
-                                                   f32x4_t (&acc)[MT][NT], int mt_active,
-                                                   int lane, int g, const UnpackConsts &magic)
+    template <int MTA>
+    static __device__ __forceinline__ void compute(const unsigned char *st, const Ctx &cx,
+                                                   f32x4_t (&acc)[MTA][NT],
+                                                   const UnpackConsts &magic)
     {
+        const int lane = cx.lane, g = cx.g, c = lane & 15;
+        const unsigned char *bw = st + B_OFF + cx.wave * B_WAVE;
+        const unsigned char *sw = st + SC_OFF + cx.wave * SC_WAVE;
 #pragma unroll
         for (int G = 0; G < GPC; ++G) {
             bf16x8_t bf[NT][S];
             float sc[NT];
+            const u32x4_t sp = *reinterpret_cast<const u32x4_t *>(sw + G * 256 + c * 16);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
+                uint32_t q[NDW];
+                const unsigned char *src = bw + (j * GPC + G) * 64 * NDW * 4;
+                if constexpr (NDW == 4) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src + lane * 16);
+                    q[0] = v[0];
+                    q[1] = v[1];
+                    q[2] = v[2];
+                    q[3] = v[3];
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NDW; ++h)
+                        q[h] = *reinterpret_cast<const uint32_t *>(src + h * 256 + lane * 4);
+                }
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    bf[j][s] = unpack<BITS, GS, NDW>(bs.q[j][G], s, g, magic);
-                sc[j] = f16_to_f32(bs.s[j][G]);
+                    bf[j][s] = unpack<BITS, GS, NDW>(q, s, g, magic);
+                sc[j] = f16_to_f32((uint16_t)(sp[j] & 0xffffu));
             }
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                if (i >= mt_active)
-                    continue;
+            for (int i = 0; i < MTA; ++i) {
                 bf16x8_t af[S];
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    af[s] = __builtin_bit_cast(bf16x8_t, sh.a[buf][(i * 4 + G * S + s) * 64 + lane]);
-                const f32x4_t nb =
-                    *reinterpret_cast<const f32x4_t *>(&sh.nbias[buf][(i * GPC + G) * 16 + 4 * g]);
+                    af[s] = *reinterpret_cast<const bf16x8_t *>(
+                        st + A_OFF + ((i * 4 + G * S + s) * 64 + lane) * 16);
+                const f32x4_t nb = *reinterpret_cast<const f32x4_t *>(
+                    st + BIAS_OFF + ((i * GPC + G) * 16 + 4 * g) * 4);
                 f32x4_t accg[NT];
 #pragma unroll
                 for (int s = 0; s < S; ++s)
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
                         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            af[s], bf[j][s], s == 0 ? nb : accg[j], 0, 0, 0);
+                            af[s], bf[j][s], s == 0 ? -nb : accg[j], 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -525,126 +622,142 @@ struct Tile {
 
     static __device__ void run(const GemmArgs &args)
     {
-        __shared__ __align__(16) Shared sh;
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int c = lane & 15, g = lane >> 4;
+        __shared__ __align__(16) unsigned char ring[STAGES * STAGE];
+        __shared__ Rows rows;
+        Ctx cx;
+        cx.tid = threadIdx.x;
+        cx.lane = cx.tid & 63;
+        cx.wave = __builtin_amdgcn_readfirstlane(cx.tid >> 6);
+        cx.g = cx.lane >> 4;
+        const int tid = cx.tid, c = cx.lane & 15;
 
         // (tile, column block) item of this workgroup
         const int nblk = (args.N + OUTC - 1) / OUTC;
         const int total = *args.num_tiles * nblk;
         const int per = (total + kXcds - 1) / kXcds;
-        const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-        const int item = xcd * per + j;
-        if (j >= per || item >= total)
+        const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+        const int item = xcd * per + jx;
+        if (jx >= per || item >= total)
             return;
-        const int b = item / nblk, nb = item % nblk;
+        cx.b = item / nblk;
+        cx.nb = item % nblk;
+        const int b = cx.b;
         const int e = args.tile_expert[b];
 
         if (tid < 64) {
             const int p = args.sorted_ids[b * BM + tid];
             const bool real = p < args.P;
             const int src0 = W13 ? args.sorted_ids[b * BM] / args.topk : b * BM;
-            sh.row_pair[tid] = p;
-            // padding rows read row 0's data: their results are never stored
-            sh.row_src[tid] = real ? (W13 ? p / args.topk : b * BM + tid) : src0;
+            rows.pair[tid] = p;
+            // padding rows copy row 0's data: their results are never stored
+            rows.src[tid] = real ? (W13 ? p / args.topk : b * BM + tid) : src0;
             const uint64_t m = __ballot(real);
             if (tid == 0)
-                sh.rows_real = __popcll(m);
+                rows.real = __popcll(m);
         }
         __syncthreads();
-        const int rows_real = sh.rows_real;
-        const int mt_active = (rows_real + 15) >> 4;
         const int K = args.K;
         const int ngroups = K / GS;
-
-        // activation rows this thread stages, and the bias row
-        const uint16_t *arow[MT];
+        cx.a = args.a;
+        cx.bias = args.a_bias;
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-            arow[i] = args.a + (size_t)sh.row_src[i * 16 + (tid & 15)] * K;
-        const int brow_r = (tid / (GPC * 16)) * 16 + (tid & 15);
-        const float *brow = args.a_bias + (size_t)sh.row_src[brow_r < BM ? brow_r : 0] * ngroups;
-
-        // this lane's weight rows (a wave past the last column stays idle but
-        // keeps taking part in the staging and the barriers)
-        const int nrows = W13 ? 2 * args.N : args.N;
-        const int col0 = nb * OUTC + wave * (W13 ? NT / 2 : NT) * 16;
-        const bool wave_on = col0 < args.N;
-        const int kw = K * BITS / 32;
-        const uint32_t *crow[NT];
-        const uint16_t *srow[NT];
-#pragma unroll
-        for (int jj = 0; jj < NT; ++jj) {
-            int n;
-            if constexpr (W13)
-                n = col0 + (jj % (NT / 2)) * 16 + c + (jj >= NT / 2 ? args.N : 0);
-            else
-                n = col0 + jj * 16 + c;
-            n = wave_on ? n : 0;
-            const size_t row = (size_t)e * nrows + n;
-            crow[jj] = args.codes + row * kw;
-            srow[jj] = args.scales + row * ngroups;
+            cx.aoff[i] = (uint32_t)rows.src[i * 16 + c] * (uint32_t)K * 2u;
+        {
+            const int ent = cx.wave * 64 + cx.lane;              // [subtile][group][row]
+            const int r = (ent / (GPC * 16)) * 16 + (ent & 15);
+            cx.boff = (uint32_t)rows.src[r < BM ? r : 0] * (uint32_t)ngroups * 4u;
         }
+        cx.ring = lds_address(ring);
 
-        f32x4_t acc[MT][NT];
+        // weight rows of this wave; a wave past the last column stays idle but
+        // keeps copying (valid rows) and taking part in the barriers
+        const int nrows = W13 ? 2 * args.N : args.N;
+        cx.col0 = cx.nb * OUTC + cx.wave * (W13 ? NT / 2 : NT) * 16;
+        cx.wave_on = cx.col0 < args.N;
+        const uint32_t kw = (uint32_t)(K * BITS / 32);
+        cx.codes = args.codes + (size_t)e * nrows * kw;
+        cx.scales = args.scales + (size_t)e * nrows * ngroups;
+        auto wrow = [&](int j, int cc) -> uint32_t {
+            if (!cx.wave_on)
+                return 0u;
+            if constexpr (W13)
+                return (uint32_t)(cx.col0 + (j % (NT / 2)) * 16 + cc + (j >= NT / 2 ? args.N : 0));
+            else
+                return (uint32_t)(cx.col0 + j * 16 + cc);
+        };
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int j = 0; j < NT; ++j)
+            cx.coff[j] = wrow(j, c) * kw * 4u;
+        cx.soff = wrow(cx.lane & 3, cx.lane >> 2) * (uint32_t)ngroups * 2u;
+
+        switch ((rows.real + 15) >> 4) {
+        case 1: body<1>(ring, rows, args, cx); break;
+        case 2: body<2>(ring, rows, args, cx); break;
+        case 3: body<3>(ring, rows, args, cx); break;
+        default: body<4>(ring, rows, args, cx); break;
+        }
+    }
+
+    // The K loop and epilogue for a tile with MTA active 16-row subtiles.
+    // Chunk kc lives in stage kc % STAGES; the copies of chunk kc + STAGES - 1
+    // are issued right after the barrier that ends the reads of chunk kc - 1.
+    template <int MTA>
+    static __device__ void body(unsigned char *ring, const Rows &rows, const GemmArgs &args,
+                                const Ctx &cx)
+    {
+        constexpr int L = copies<MTA>();
+        static_assert((STAGES - 1) * L < 64, "copies in flight exceed the wait counter");
+        f32x4_t acc[MTA][NT];
 #pragma unroll
-            for (int jj = 0; jj < NT; ++jj)
-                acc[i][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < MTA; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         const UnpackConsts magic = unpack_consts();
-        const int nchunks = K / KC;
-        const int mt_w = wave_on ? mt_active : 0;   // subtiles this wave multiplies
-        AStage as;
-        BStage b0, b1;
-        load_a(as, arow, brow, 0, mt_active, tid);
-        if (wave_on)
-            load_b(b0, crow, srow, 0, g);
-        store_a(sh, 0, as, mt_active, tid);
-        __syncthreads();
-        for (int kc = 0; kc < nchunks; kc += 2) {
-            if (kc + 1 < nchunks) {
-                load_a(as, arow, brow, kc + 1, mt_active, tid);
-                if (wave_on)
-                    load_b(b1, crow, srow, kc + 1, g);
-            }
-            compute(sh, 0, b0, acc, mt_w, lane, g, magic);
-            if (kc + 1 < nchunks)
-                store_a(sh, 1, as, mt_active, tid);
-            __syncthreads();
-            if (kc + 1 < nchunks) {
-                if (kc + 2 < nchunks) {
-                    load_a(as, arow, brow, kc + 2, mt_active, tid);
-                    if (wave_on)
-                        load_b(b0, crow, srow, kc + 2, g);
-                }
-                compute(sh, 1, b1, acc, mt_w, lane, g, magic);
-                if (kc + 2 < nchunks)
-                    store_a(sh, 0, as, mt_active, tid);
-                __syncthreads();
-            }
+        const int nchunks = args.K / KC;
+#pragma unroll
+        for (int p = 0; p < STAGES - 1; ++p)
+            if (p < nchunks)
+                issue<MTA>(p, cx, p);
+        for (int kc = 0; kc < nchunks; ++kc) {
+            // this wave's copies of chunk kc have landed (later chunks may not have)
+            if (STAGES == 3 && kc + 1 < nchunks)
+                wait_vm<(STAGES - 2) * L>();
+            else
+                wait_vm<0>();
+            workgroup_barrier();
+            const int nx = kc + STAGES - 1;
+            if (nx < nchunks)
+                issue<MTA>(nx % STAGES, cx, nx);
+            if (cx.wave_on)
+                compute<MTA>(ring + (kc % STAGES) * STAGE, cx, acc, magic);
         }
+        __syncthreads();   // every wave is done with the ring
 
+        const int rows_real = rows.real;
         if constexpr (W13) {
-            epilogue_w13(sh, args, acc, b, nb, wave, c, g, rows_real, mt_w, tid);
+            epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(ring), args, acc, cx, rows_real);
         } else {
+            if (!cx.wave_on)
+                return;
+            const int g = cx.g;
             // routing-weighted scatter-add into the FP32 accumulator
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                if (i >= mt_w)
-                    continue;
+            for (int i = 0; i < MTA; ++i) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int r = 16 * i + 4 * g + v;
                     if (r >= rows_real)
                         continue;
-                    const int p = sh.row_pair[r];
+                    const int p = rows.pair[r];
                     const float w = args.topk_w[p];
-                    float *orow = args.out_f32 + (size_t)(p / args.topk) * args.N + col0 + c;
+                    float *orow =
+                        args.out_f32 + (size_t)(p / args.topk) * args.N + cx.col0 + (cx.lane & 15);
 #pragma unroll
-                    for (int jj = 0; jj < NT; ++jj)
-                        unsafeAtomicAdd(orow + jj * 16, w * acc[i][jj][v]);
+                    for (int j = 0; j < NT; ++j)
+                        unsafeAtomicAdd(orow + j * 16, w * acc[i][j][v]);
                 }
             }
         }
@@ -653,64 +766,74 @@ struct Tile {
     // SwiGLU on matching gate/up columns; BF16 act rows written in the w2
     // fragment order (scaled per frag_shift), with the per-group bias term of
     // each (row, w2 group): the workgroup covers whole w2 groups (gs2 <= 128).
-    static __device__ __forceinline__ void epilogue_w13(Shared &sh, const GemmArgs &args,
-                                                        const f32x4_t (&acc)[MT][NT], int b,
-                                                        int nb, int wave, int c, int g,
-                                                        int rows_real, int mt_w, int tid)
+    template <int MTA>
+    static __device__ __forceinline__ void epilogue_w13(EpiW13 *epi, const GemmArgs &args,
+                                                        const f32x4_t (&acc)[MTA][NT],
+                                                        const Ctx &cx, int rows_real)
     {
         constexpr int NG = NT / 2;
-        // the union's act tile overlays the A buffers: the loop's last barrier
-        // has already been passed by every wave
+        const int c = cx.lane & 15, g = cx.g;
+        if (cx.wave_on) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            if (i >= mt_w)
-                continue;
+            for (int i = 0; i < MTA; ++i)
 #pragma unroll
-            for (int jj = 0; jj < NG; ++jj)
+                for (int j = 0; j < NG; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float a = swiglu(acc[i][jj][v], acc[i][NG + jj][v], args.alpha,
-                                           args.beta, args.clamp);
-                    sh.epi.act[(16 * i + 4 * g + v) * ACT_STRIDE + wave * NG * 16 + jj * 16 + c] =
-                        f32_to_bf16(a);
-                }
+                    for (int v = 0; v < 4; ++v) {
+                        const float a = swiglu(acc[i][j][v], acc[i][NG + j][v], args.alpha,
+                                               args.beta, args.clamp);
+                        epi->act[(16 * i + 4 * g + v) * ACT_STRIDE + cx.wave * NG * 16 + j * 16 +
+                                 c] = f32_to_bf16(a);
+                    }
         }
         __syncthreads();
-        const int gs2 = args.gs_next, bits2 = args.bits_next;
-        const int ncols = min(OUTC, args.N - nb * OUTC);
+        switch (args.bits_next * 1000 + args.gs_next) {
+        case 2032: act_out<2, 32>(epi, args, cx, rows_real); break;
+        case 2064: act_out<2, 64>(epi, args, cx, rows_real); break;
+        case 2128: act_out<2, 128>(epi, args, cx, rows_real); break;
+        case 4032: act_out<4, 32>(epi, args, cx, rows_real); break;
+        case 4064: act_out<4, 64>(epi, args, cx, rows_real); break;
+        default: act_out<4, 128>(epi, args, cx, rows_real); break;
+        }
+    }
+
+    template <int B2, int G2>
+    static __device__ __forceinline__ void act_out(EpiW13 *epi, const GemmArgs &args,
+                                                   const Ctx &cx, int rows_real)
+    {
+        const int tid = cx.tid;
+        const int ncols = min(OUTC, args.N - cx.nb * OUTC);
         const int pieces = ncols / 8;
         for (int q = tid; q < rows_real * pieces; q += NTHREADS) {
             const int r = q / pieces, c8 = q % pieces;
-            const int gl = (c8 * 8) / gs2, pos0 = (c8 * 8) % gs2;
+            const int gl = (c8 * 8) / G2, pos0 = (c8 * 8) % G2;
+            const uint16_t *arow = epi->act + r * ACT_STRIDE + gl * G2;
             u32x4_t o;
             float sum = 0.f;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const int p0 = pos0 + 2 * h, p1 = p0 + 1;
-                const uint32_t lo = bf16_scaled(
-                    sh.epi.act[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p0)],
-                    frag_shift(bits2, gs2, p0));
-                const uint32_t hi = bf16_scaled(
-                    sh.epi.act[r * ACT_STRIDE + gl * gs2 + frag_src(bits2, gs2, p1)],
-                    frag_shift(bits2, gs2, p1));
-                sum += bf16_to_f32(lo) * (float)frag_bias_weight(bits2, gs2, p0);
-                sum += bf16_to_f32(hi) * (float)frag_bias_weight(bits2, gs2, p1);
+                const uint32_t lo = bf16_scaled(arow[frag_src(B2, G2, p0)], frag_shift(B2, G2, p0));
+                const uint32_t hi = bf16_scaled(arow[frag_src(B2, G2, p1)], frag_shift(B2, G2, p1));
+                sum += bf16_to_f32(lo) * (float)frag_bias_weight(B2, G2, p0);
+                sum += bf16_to_f32(hi) * (float)frag_bias_weight(B2, G2, p1);
                 o[h] = lo | (hi << 16);
             }
-            *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(b * BM + r) * args.N +
-                                         nb * OUTC + c8 * 8) = o;
-            sh.epi.part[r * (OUTC / 8) + c8] = sum;
+            *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(cx.b * BM + r) * args.N +
+                                         cx.nb * OUTC + c8 * 8) = o;
+            epi->part[r * (OUTC / 8) + c8] = sum;
         }
         __syncthreads();
-        const int gpb = ncols / gs2;  // w2 groups in this workgroup
-        const int per = gs2 / 8;
-        const int ngroups2 = args.N / gs2;
+        constexpr int per = G2 / 8;
+        const int gpb = ncols / G2;  // w2 groups in this workgroup
+        const int ngroups2 = args.N / G2;
         for (int q = tid; q < rows_real * gpb; q += NTHREADS) {
             const int r = q / gpb, gl = q % gpb;
             float sum = 0.f;
+#pragma unroll
             for (int k = 0; k < per; ++k)
-                sum += sh.epi.part[r * (OUTC / 8) + gl * per + k];
-            args.act_bias_out[(size_t)(b * BM + r) * ngroups2 + nb * (OUTC / gs2) + gl] = sum;
+                sum += epi->part[r * (OUTC / 8) + gl * per + k];
+            args.act_bias_out[(size_t)(cx.b * BM + r) * ngroups2 + cx.nb * (OUTC / G2) + gl] = sum;
         }
     }
 };
