@@ -140,6 +140,12 @@ SMALL = {
     "pre_15_16_17_rows": (spec(T=40, H=256, I=128, E=8, topk=2), "151617", PRE),
     "pre_single_expert": (spec(T=5, E=1, topk=1), None, PRE),
     "pre_threshold_bm64_exact": (spec(T=64, H=256, I=128, E=4, topk=1), None, PRE),
+    # 64 and 48 groups per row: the scale/bias staging runs in two segments
+    "pre_g32_two_segments": (spec(T=48, H=2048, I=1536, E=3, topk=2, bits13=4, group13=32,
+                                  bits2=2, group2=32, **ACT), None, PRE),
+    # H = 640: the last w2 column block is partly idle (640 = 512 + 128)
+    "pre_w2_partial_column_block": (spec(T=64, H=640, I=384, E=3, topk=2, bits13=2,
+                                         group13=64, bits2=4, group2=128), None, PRE),
 }
 
 

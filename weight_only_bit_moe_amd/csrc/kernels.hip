@@ -448,31 +448,34 @@ __device__ __forceinline__ void copy_to_lds(const void *base, uint32_t voff, uin
 
 template <int BITS, int GS, bool W13>
 struct Tile {
-    static constexpr int BM = 64, MT = 4, NT = 4, NW = 4, NTHREADS = NW * 64;
-    static constexpr int BN = NW * NT * 16;          // weight rows per workgroup
+    static constexpr int BM = 64, MT = 4, NT = 4, NW = 8, NTHREADS = NW * 64;
+    static constexpr int BN = NW * NT * 16;          // weight rows per workgroup (512)
     static constexpr int OUTC = W13 ? BN / 2 : BN;   // output columns per workgroup
     static constexpr int KC = 128;                   // K per chunk
     static constexpr int GPC = KC / GS;              // groups per chunk
     static constexpr int S = GS / 32;                // MFMA steps per group
     static constexpr int NDW = CodeTraits<BITS, GS>::NDW;
-    static constexpr int NDWI = NDW == 4 ? 1 : NDW;  // code copies per (subtile, group)
+    static constexpr int RB = KC * BITS / 8;         // code bytes of one row per chunk
+    static constexpr int PIECES = RB / 16;           // 16-byte pieces per row and chunk
+    static constexpr int SEGG = 32;                  // groups per scale/bias segment
     static constexpr int ACT_STRIDE = OUTC + 8;      // W13 epilogue tile, bf16 elements
     static constexpr int kXcds = 8;
 
-    // One pipeline stage in LDS, every piece in the order the MFMA lanes read it:
-    //   A      [subtile][step][lane] 16 bytes           16 KB
-    //   bias   [subtile][group][row] floats (negated)    1 KB
-    //   codes  [wave][subtile][group][copy][lane] NDW/NDWI dwords
-    //   scales [wave][group][column][subtile] dword slots (value in the low half)
+    // LDS:
+    //   scales [group in segment][wave][column][subtile] halves         32 KB
+    //   bias   [group in segment][row] floats, negated                   8 KB
+    //   ring of STAGES stages, each
+    //     A     [subtile][step][lane] 16-byte MFMA fragments            16 KB
+    //     codes [wave][subtile row][RB bytes], 16-byte pieces swizzled  NW*64*RB
+    static constexpr int SC_BYTES = SEGG * NW * 64 * 2;
+    static constexpr int BI_OFF = SC_BYTES;
+    static constexpr int RING_OFF = BI_OFF + SEGG * BM * 4;
     static constexpr int A_OFF = 0;
-    static constexpr int BIAS_OFF = A_OFF + MT * 4 * 64 * 16;
-    static constexpr int B_WAVE = NT * GPC * 64 * NDW * 4;
-    static constexpr int B_OFF = BIAS_OFF + 256 * 4;
-    static constexpr int SC_WAVE = GPC * 64 * 4;
-    static constexpr int SC_OFF = B_OFF + NW * B_WAVE;
-    static constexpr int STAGE = SC_OFF + NW * SC_WAVE;
-    // deepest ring that leaves room for two workgroups per CU
-    static constexpr int STAGES = 3 * STAGE + 1024 <= 80 * 1024 ? 3 : 2;
+    static constexpr int B_OFF = MT * 4 * 64 * 16;
+    static constexpr int B_WAVE = 64 * RB;
+    static constexpr int STAGE = B_OFF + NW * B_WAVE;
+    static constexpr int STAGES = RING_OFF + 3 * STAGE <= 150 * 1024 ? 3 : 2;
+    static constexpr int LDS_BYTES = RING_OFF + STAGES * STAGE;
 
     struct EpiW13 {
         uint16_t act[BM * ACT_STRIDE];
@@ -485,32 +488,28 @@ struct Tile {
         int real;
     };
 
+    // 16-byte piece position inside a row's chunk of codes: XOR-swizzled so
+    // that the 8 (or 16) lanes of one LDS access phase hit distinct banks.
+    static __host__ __device__ constexpr int swz(int row) { return PIECES == 4 ? (row >> 1) & 3 : (row >> 2) & 1; }
+
     // Per-lane copy sources: 32-bit byte offsets from workgroup-uniform
     // bases.  Padding rows and idle waves point at valid rows.
     struct Ctx {
         const uint16_t *a;
-        const float *bias;
         const uint32_t *codes;      // this expert's codes
-        const uint16_t *scales;     // this expert's scales
-        uint32_t aoff[MT];          // activation row of subtile i this lane copies
-        uint32_t boff;              // bias row this lane copies
-        uint32_t coff[NT];          // this lane's weight row in subtile j
-        uint32_t soff;              // weight row whose scales this lane copies
+        uint32_t aoff[2];           // activation rows of the A pieces this lane copies
+        uint32_t akoff[2];          // their K offset inside a chunk (bytes)
+        uint32_t coff[4];           // code rows this lane copies (byte offsets)
         uint32_t ring;              // LDS address of the ring
         int b, nb, col0, tid, lane, wave, g;
         bool wave_on;
     };
 
-    // Barrier with no memory fence, so the copies of later chunks stay in
-    // flight.  This wave's LDS reads are complete before it (lgkmcnt(0)), and
-    // the asm's memory clobber keeps the compiler from moving LDS accesses
-    // across it.
     static __device__ __forceinline__ void workgroup_barrier()
     {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
-    // vmcnt(n) alone (expcnt and lgkmcnt left at their maximum)
     template <int N>
     static __device__ __forceinline__ void wait_vm()
     {
@@ -518,82 +517,70 @@ struct Tile {
         __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     }
 
-    // number of copies each wave issues per chunk
+    // A pieces each wave copies per chunk (16 slots shared by 8 waves; slots of
+    // inactive subtiles get harmless copies so every wave issues the same number)
     template <int MTA>
-    static constexpr int copies() { return MTA + 1 + NT * GPC * NDWI + GPC; }
+    static constexpr int a_copies() { return MTA <= 2 ? 1 : 2; }
+    static constexpr int code_copies() { return 64 * PIECES / 64; }   // = PIECES
+    template <int MTA>
+    static constexpr int copies() { return a_copies<MTA>() + code_copies(); }
 
-    // Issue every copy of chunk kc into LDS stage `st` (wave-uniform pointers;
-    // lane l's data lands at ptr + l * size).
     template <int MTA>
     static __device__ __forceinline__ void issue(int stage, const Ctx &cx, int kc)
     {
-        const int l = cx.lane;
         const uint32_t st = cx.ring + stage * STAGE;
-        // activations: this wave copies step `wave` of every active subtile
-        const uint32_t koff = (uint32_t)(kc * KC + cx.wave * 32 + (l >> 4) * 8) * 2u;
 #pragma unroll
-        for (int i = 0; i < MTA; ++i)
-            copy_to_lds<16>(cx.a, cx.aoff[i] + koff, st + A_OFF + (i * 4 + cx.wave) * 64 * 16);
-        // bias terms: entries [64 * wave, 64 * wave + 64) of [subtile][group][row]
-        copy_to_lds<4>(cx.bias,
-                       cx.boff + (uint32_t)(kc * GPC + ((cx.wave * 64 + l) >> 4) % GPC) * 4u,
-                       st + BIAS_OFF + cx.wave * 256);
-        // codes of this wave's weight rows
+        for (int k = 0; k < a_copies<MTA>(); ++k) {
+            const int slot = cx.wave + NW * k;   // [subtile][step]
+            copy_to_lds<16>(cx.a, cx.aoff[k] + cx.akoff[k] + (uint32_t)kc * (KC * 2),
+                            st + A_OFF + slot * 64 * 16);
+        }
         const uint32_t bw = st + B_OFF + cx.wave * B_WAVE;
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int G = 0; G < GPC; ++G) {
-                const uint32_t src =
-                    cx.coff[j] + (uint32_t)CodeTraits<BITS, GS>::dword_off(kc * GPC + G, cx.g) * 4u;
-                const uint32_t dst = bw + (j * GPC + G) * 64 * NDW * 4;
-                if constexpr (NDW == 4) {
-                    copy_to_lds<16>(cx.codes, src, dst);
-                } else {
-#pragma unroll
-                    for (int h = 0; h < NDWI; ++h)
-                        copy_to_lds<4>(cx.codes, src + h * 4, dst + h * 256);
-                }
-            }
-        // scales: lane l copies column l / 4 of subtile l % 4
-        const uint32_t sw = st + SC_OFF + cx.wave * SC_WAVE;
-#pragma unroll
-        for (int G = 0; G < GPC; ++G)
-            copy_to_lds<2>(cx.scales, cx.soff + (uint32_t)(kc * GPC + G) * 2u, sw + G * 256);
+        for (int k = 0; k < code_copies(); ++k)
+            copy_to_lds<16>(cx.codes, cx.coff[k] + (uint32_t)kc * RB, bw + k * 64 * 16);
     }
 
     template <int MTA>
-    static __device__ __forceinline__ void compute(const unsigned char *st, const Ctx &cx,
+    static __device__ __forceinline__ void compute(const unsigned char *lds, int stage, int kc,
+                                                   int seg_g0, const Ctx &cx,
                                                    f32x4_t (&acc)[MTA][NT],
                                                    const UnpackConsts &magic)
     {
         const int lane = cx.lane, g = cx.g, c = lane & 15;
+        const unsigned char *st = lds + RING_OFF + stage * STAGE;
         const unsigned char *bw = st + B_OFF + cx.wave * B_WAVE;
-        const unsigned char *sw = st + SC_OFF + cx.wave * SC_WAVE;
 #pragma unroll
         for (int G = 0; G < GPC; ++G) {
+            const int Gs = kc * GPC + G - seg_g0;   // group inside the segment
             bf16x8_t bf[NT][S];
             float sc[NT];
-            const u32x4_t sp = *reinterpret_cast<const u32x4_t *>(sw + G * 256 + c * 16);
+            const u32x2_t sp =
+                *reinterpret_cast<const u32x2_t *>(lds + ((Gs * NW + cx.wave) * 64 + c * 4) * 2);
+            const int off = CodeTraits<BITS, GS>::dword_off(G, g) * 4;   // inside the row's chunk
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
+                const int row = j * 16 + c;
+                const unsigned char *src =
+                    bw + row * RB + (((off >> 4) ^ swz(row)) << 4) + (off & 15);
                 uint32_t q[NDW];
-                const unsigned char *src = bw + (j * GPC + G) * 64 * NDW * 4;
                 if constexpr (NDW == 4) {
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src + lane * 16);
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
                     q[0] = v[0];
                     q[1] = v[1];
                     q[2] = v[2];
                     q[3] = v[3];
+                } else if constexpr (NDW == 2) {
+                    const u32x2_t v = *reinterpret_cast<const u32x2_t *>(src);
+                    q[0] = v[0];
+                    q[1] = v[1];
                 } else {
-#pragma unroll
-                    for (int h = 0; h < NDW; ++h)
-                        q[h] = *reinterpret_cast<const uint32_t *>(src + h * 256 + lane * 4);
+                    q[0] = *reinterpret_cast<const uint32_t *>(src);
                 }
 #pragma unroll
                 for (int s = 0; s < S; ++s)
                     bf[j][s] = unpack<BITS, GS, NDW>(q, s, g, magic);
-                sc[j] = f16_to_f32((uint16_t)(sp[j] & 0xffffu));
+                sc[j] = f16_to_f32((uint16_t)(sp[j >> 1] >> (16 * (j & 1))));
             }
 #pragma unroll
             for (int i = 0; i < MTA; ++i) {
@@ -603,14 +590,14 @@ struct Tile {
                     af[s] = *reinterpret_cast<const bf16x8_t *>(
                         st + A_OFF + ((i * 4 + G * S + s) * 64 + lane) * 16);
                 const f32x4_t nb = *reinterpret_cast<const f32x4_t *>(
-                    st + BIAS_OFF + ((i * GPC + G) * 16 + 4 * g) * 4);
+                    lds + BI_OFF + (Gs * BM + i * 16 + 4 * g) * 4);
                 f32x4_t accg[NT];
 #pragma unroll
                 for (int s = 0; s < S; ++s)
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
                         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            af[s], bf[j][s], s == 0 ? -nb : accg[j], 0, 0, 0);
+                            af[s], bf[j][s], s == 0 ? nb : accg[j], 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -620,16 +607,47 @@ struct Tile {
         }
     }
 
+    // Scales of the workgroup's weight rows and negated bias terms of the
+    // tile's rows for groups [g0, g0 + ng) go to LDS (plain loads: this runs
+    // once per segment, normally once per workgroup).
+    static __device__ __forceinline__ void load_segment(unsigned char *lds, const Rows &rows,
+                                                        const GemmArgs &args, const Ctx &cx,
+                                                        int e, int g0, int ng)
+    {
+        const int K = args.K, ngroups = K / GS;
+        const int nrows = W13 ? 2 * args.N : args.N;
+        const uint16_t *sbase = args.scales + (size_t)e * nrows * ngroups;
+        uint16_t *sc = reinterpret_cast<uint16_t *>(lds);
+        // consecutive lanes take consecutive groups of one weight row
+        for (int idx = cx.tid; idx < BN * ng; idx += NTHREADS) {
+            const int q = idx / ng, Gl = idx % ng;             // q = WG row in [wave][column][subtile] order
+            const int w = q >> 6, cc = (q >> 2) & 15, j = q & 3;
+            int n;
+            if constexpr (W13)
+                n = args.N * (j >> 1) + cx.nb * OUTC + w * 32 + (j & 1) * 16 + cc;
+            else
+                n = cx.nb * OUTC + w * 64 + j * 16 + cc;
+            const bool valid = W13 ? (cx.nb * OUTC + w * 32 + (j & 1) * 16 + cc) < args.N
+                                   : n < args.N;
+            sc[Gl * NW * 64 + q] = valid ? sbase[(size_t)n * ngroups + g0 + Gl] : (uint16_t)0;
+        }
+        float *bi = reinterpret_cast<float *>(lds + BI_OFF);
+        for (int idx = cx.tid; idx < BM * ng; idx += NTHREADS) {
+            const int r = idx / ng, Gl = idx % ng;
+            bi[Gl * BM + r] = -args.a_bias[(size_t)rows.src[r] * ngroups + g0 + Gl];
+        }
+    }
+
     static __device__ void run(const GemmArgs &args)
     {
-        __shared__ __align__(16) unsigned char ring[STAGES * STAGE];
+        __shared__ __align__(16) unsigned char lds[LDS_BYTES];
         __shared__ Rows rows;
         Ctx cx;
         cx.tid = threadIdx.x;
         cx.lane = cx.tid & 63;
         cx.wave = __builtin_amdgcn_readfirstlane(cx.tid >> 6);
         cx.g = cx.lane >> 4;
-        const int tid = cx.tid, c = cx.lane & 15;
+        const int tid = cx.tid, lane = cx.lane;
 
         // (tile, column block) item of this workgroup
         const int nblk = (args.N + OUTC - 1) / OUTC;
@@ -657,18 +675,15 @@ struct Tile {
         }
         __syncthreads();
         const int K = args.K;
-        const int ngroups = K / GS;
         cx.a = args.a;
-        cx.bias = args.a_bias;
+        // A pieces: slot = wave + 8k -> subtile slot / 4, step slot % 4
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-            cx.aoff[i] = (uint32_t)rows.src[i * 16 + c] * (uint32_t)K * 2u;
-        {
-            const int ent = cx.wave * 64 + cx.lane;              // [subtile][group][row]
-            const int r = (ent / (GPC * 16)) * 16 + (ent & 15);
-            cx.boff = (uint32_t)rows.src[r < BM ? r : 0] * (uint32_t)ngroups * 4u;
+        for (int k = 0; k < 2; ++k) {
+            const int slot = cx.wave + NW * k;
+            cx.aoff[k] = (uint32_t)rows.src[(slot >> 2) * 16 + (lane & 15)] * (uint32_t)K * 2u;
+            cx.akoff[k] = (uint32_t)((slot & 3) * 32 + (lane >> 4) * 8) * 2u;
         }
-        cx.ring = lds_address(ring);
+        cx.ring = lds_address(lds + RING_OFF);
 
         // weight rows of this wave; a wave past the last column stays idle but
         // keeps copying (valid rows) and taking part in the barriers
@@ -677,25 +692,28 @@ struct Tile {
         cx.wave_on = cx.col0 < args.N;
         const uint32_t kw = (uint32_t)(K * BITS / 32);
         cx.codes = args.codes + (size_t)e * nrows * kw;
-        cx.scales = args.scales + (size_t)e * nrows * ngroups;
-        auto wrow = [&](int j, int cc) -> uint32_t {
-            if (!cx.wave_on)
-                return 0u;
-            if constexpr (W13)
-                return (uint32_t)(cx.col0 + (j % (NT / 2)) * 16 + cc + (j >= NT / 2 ? args.N : 0));
-            else
-                return (uint32_t)(cx.col0 + j * 16 + cc);
-        };
+        // code copy k of this lane: 16-byte slot lane of rows [k*64/PIECES, ...)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-            cx.coff[j] = wrow(j, c) * kw * 4u;
-        cx.soff = wrow(cx.lane & 3, cx.lane >> 2) * (uint32_t)ngroups * 2u;
+        for (int k = 0; k < 4; ++k) {
+            const int slot = k * 64 + lane;                      // in [row][position]
+            const int row = slot / PIECES, pos = slot % PIECES;  // wave-local row j*16 + c
+            const int piece = pos ^ swz(row);
+            const int j = row >> 4, cc = row & 15;
+            uint32_t n = 0;
+            if (cx.wave_on && row < 64) {
+                if constexpr (W13)
+                    n = (uint32_t)(cx.col0 + (j % (NT / 2)) * 16 + cc + (j >= NT / 2 ? args.N : 0));
+                else
+                    n = (uint32_t)(cx.col0 + j * 16 + cc);
+            }
+            cx.coff[k] = n * kw * 4u + (uint32_t)piece * 16u;
+        }
 
         switch ((rows.real + 15) >> 4) {
-        case 1: body<1>(ring, rows, args, cx); break;
-        case 2: body<2>(ring, rows, args, cx); break;
-        case 3: body<3>(ring, rows, args, cx); break;
-        default: body<4>(ring, rows, args, cx); break;
+        case 1: body<1>(lds, rows, args, cx, e); break;
+        case 2: body<2>(lds, rows, args, cx, e); break;
+        case 3: body<3>(lds, rows, args, cx, e); break;
+        default: body<4>(lds, rows, args, cx, e); break;
         }
     }
 
@@ -703,8 +721,8 @@ struct Tile {
     // Chunk kc lives in stage kc % STAGES; the copies of chunk kc + STAGES - 1
     // are issued right after the barrier that ends the reads of chunk kc - 1.
     template <int MTA>
-    static __device__ void body(unsigned char *ring, const Rows &rows, const GemmArgs &args,
-                                const Ctx &cx)
+    static __device__ void body(unsigned char *lds, const Rows &rows, const GemmArgs &args,
+                                const Ctx &cx, int e)
     {
         constexpr int L = copies<MTA>();
         static_assert((STAGES - 1) * L < 64, "copies in flight exceed the wait counter");
@@ -717,11 +735,19 @@ struct Tile {
 
         const UnpackConsts magic = unpack_consts();
         const int nchunks = args.K / KC;
+        const int ngroups = args.K / GS;
+        constexpr int SEGC = SEGG / GPC;   // chunks per segment
 #pragma unroll
         for (int p = 0; p < STAGES - 1; ++p)
             if (p < nchunks)
                 issue<MTA>(p, cx, p);
         for (int kc = 0; kc < nchunks; ++kc) {
+            if (kc % SEGC == 0) {
+                // new scale/bias segment: everyone is done with the previous one
+                workgroup_barrier();
+                const int g0 = kc * GPC;
+                load_segment(lds, rows, args, cx, e, g0, min(SEGG, ngroups - g0));
+            }
             // this wave's copies of chunk kc have landed (later chunks may not have)
             if (STAGES == 3 && kc + 1 < nchunks)
                 wait_vm<(STAGES - 2) * L>();
@@ -732,13 +758,14 @@ struct Tile {
             if (nx < nchunks)
                 issue<MTA>(nx % STAGES, cx, nx);
             if (cx.wave_on)
-                compute<MTA>(ring + (kc % STAGES) * STAGE, cx, acc, magic);
+                compute<MTA>(lds, kc % STAGES, kc, (kc / SEGC) * SEGG, cx, acc, magic);
         }
         __syncthreads();   // every wave is done with the ring
 
         const int rows_real = rows.real;
         if constexpr (W13) {
-            epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(ring), args, acc, cx, rows_real);
+            epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(lds + RING_OFF), args, acc, cx,
+                              rows_real);
         } else {
             if (!cx.wave_on)
                 return;
@@ -839,7 +866,7 @@ struct Tile {
 };
 
 template <int BITS, int GS, bool W13>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tile_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void tile_kernel(
     const GemmArgs args)
 {
     Tile<BITS, GS, W13>::run(args);
