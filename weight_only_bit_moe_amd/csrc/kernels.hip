@@ -428,9 +428,17 @@ __device__ __forceinline__ uint32_t lds_address(const void *p)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int BYTES>
-__device__ __forceinline__ void copy_to_lds(const void *base, uint32_t voff, uint32_t lds_in)
+__device__ __forceinline__ void copy_to_lds(const void *base_in, uint32_t voff, uint32_t lds_in)
 {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+    // both are wave-uniform by construction; make that explicit for the
+    // scalar-register operands
+    // (readfirstlane returns int: cast to uint32_t before widening, or a low
+    // half with bit 31 set would be sign-extended into the high half)
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_in);
+    const uint64_t b64 = reinterpret_cast<uintptr_t>(base_in);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
+    const void *base = reinterpret_cast<const void *>(((uint64_t)hi << 32) | (uint64_t)lo);
     if constexpr (BYTES == 16)
         asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
                      "s"(lds)
@@ -608,8 +616,24 @@ struct Tile {
     }
 
     // Scales of the workgroup's weight rows and negated bias terms of the
-    // tile's rows for groups [g0, g0 + ng) go to LDS (plain loads: this runs
-    // once per segment, normally once per workgroup).
+    // tile's rows for groups [g0, g0 + ng) go to LDS.  Plain loads, issued
+    // in batches so their latencies overlap; this runs once per segment
+    // (normally once per workgroup).
+    static __device__ __forceinline__ int wg_row(const GemmArgs &args, int nb, int q, bool &valid)
+    {
+        // q = workgroup weight row in [wave][column][subtile] order
+        const int w = q >> 6, cc = (q >> 2) & 15, j = q & 3;
+        if constexpr (W13) {
+            const int col = nb * OUTC + w * 32 + (j & 1) * 16 + cc;
+            valid = col < args.N;
+            return args.N * (j >> 1) + col;
+        } else {
+            const int n = nb * OUTC + w * 64 + j * 16 + cc;
+            valid = n < args.N;
+            return n;
+        }
+    }
+
     static __device__ __forceinline__ void load_segment(unsigned char *lds, const Rows &rows,
                                                         const GemmArgs &args, const Ctx &cx,
                                                         int e, int g0, int ng)
@@ -618,23 +642,69 @@ struct Tile {
         const int nrows = W13 ? 2 * args.N : args.N;
         const uint16_t *sbase = args.scales + (size_t)e * nrows * ngroups;
         uint16_t *sc = reinterpret_cast<uint16_t *>(lds);
-        // consecutive lanes take consecutive groups of one weight row
-        for (int idx = cx.tid; idx < BN * ng; idx += NTHREADS) {
-            const int q = idx / ng, Gl = idx % ng;             // q = WG row in [wave][column][subtile] order
-            const int w = q >> 6, cc = (q >> 2) & 15, j = q & 3;
-            int n;
-            if constexpr (W13)
-                n = args.N * (j >> 1) + cx.nb * OUTC + w * 32 + (j & 1) * 16 + cc;
-            else
-                n = cx.nb * OUTC + w * 64 + j * 16 + cc;
-            const bool valid = W13 ? (cx.nb * OUTC + w * 32 + (j & 1) * 16 + cc) < args.N
-                                   : n < args.N;
-            sc[Gl * NW * 64 + q] = valid ? sbase[(size_t)n * ngroups + g0 + Gl] : (uint16_t)0;
-        }
         float *bi = reinterpret_cast<float *>(lds + BI_OFF);
-        for (int idx = cx.tid; idx < BM * ng; idx += NTHREADS) {
-            const int r = idx / ng, Gl = idx % ng;
-            bi[Gl * BM + r] = -args.a_bias[(size_t)rows.src[r] * ngroups + g0 + Gl];
+        const bool vec = ng == SEGG && ngroups % 8 == 0 && g0 % 8 == 0 &&
+                         reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
+        if (vec) {
+            // 16-byte pieces: 8 groups of one weight row; 512 rows x 4 pieces
+            constexpr int PER = BN * (SEGG / 8) / NTHREADS;
+            u32x4_t v[PER];
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int idx = cx.tid + k * NTHREADS;
+                const int q = idx / (SEGG / 8), pc = idx % (SEGG / 8);
+                bool valid;
+                const int n = wg_row(args, cx.nb, q, valid);
+                v[k] = valid ? *reinterpret_cast<const u32x4_t *>(
+                                   sbase + (size_t)n * ngroups + g0 + pc * 8)
+                             : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int idx = cx.tid + k * NTHREADS;
+                const int q = idx / (SEGG / 8), pc = idx % (SEGG / 8);
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    sc[(pc * 8 + h) * BN + q] = (uint16_t)(v[k][h >> 1] >> (16 * (h & 1)));
+            }
+        } else {
+            // any alignment: 8 halves per thread and batch
+            for (int base = 0; base < BN * ng; base += 8 * NTHREADS) {
+                uint16_t h[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int idx = base + cx.tid + k * NTHREADS;
+                    const int q = idx / ng, Gl = idx % ng;
+                    bool valid;
+                    const int n = wg_row(args, cx.nb, q < BN ? q : 0, valid);
+                    h[k] = (idx < BN * ng && valid) ? sbase[(size_t)n * ngroups + g0 + Gl]
+                                                    : (uint16_t)0;
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int idx = base + cx.tid + k * NTHREADS;
+                    if (idx < BN * ng)
+                        sc[(idx % ng) * BN + idx / ng] = h[k];
+                }
+            }
+        }
+        // bias terms: 64 rows x ng floats; 4 groups per 16-byte piece when possible
+        if (ng % 4 == 0 && ngroups % 4 == 0 && g0 % 4 == 0) {
+            const int pieces = BM * (ng / 4);   // <= 512
+            const int idx = cx.tid;
+            if (idx < pieces) {
+                const int r = idx / (ng / 4), pc = idx % (ng / 4);
+                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(
+                    args.a_bias + (size_t)rows.src[r] * ngroups + g0 + pc * 4);
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    bi[(pc * 4 + h) * BM + r] = -v[h];
+            }
+        } else {
+            for (int idx = cx.tid; idx < BM * ng; idx += NTHREADS) {
+                const int r = idx / ng, Gl = idx % ng;
+                bi[Gl * BM + r] = -args.a_bias[(size_t)rows.src[r] * ngroups + g0 + Gl];
+            }
         }
     }
 
