@@ -64,6 +64,10 @@ def _align_cases():
     cases.append(("bad_ids", ids, 16))
     cases.append(("one_hot_expert", np.full((1500, 2), 7), 256))
     cases.append(("max_experts", rng.integers(0, 1024, size=(4096, 8)), 1024))
+    # several workgroups (4096 pairs each): invalid ids, exact and ragged chunk ends
+    cases.append(("bad_ids_multi_block", rng.integers(-3, 20, size=(3000, 4)), 16))
+    cases.append(("exact_two_chunks", rng.integers(0, 64, size=(1024, 8)), 64))
+    cases.append(("chunk_plus_one", rng.integers(0, 8, size=(4097, 1)), 8))
     return cases
 
 

@@ -47,7 +47,7 @@ int check_sizes(int T, int H, int I, int E, int topk)
 }
 
 struct Layout {
-    size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, total;
+    size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, ccounts, total;
 };
 
 Layout layout_of(int T, int H, int I, int E, int topk)
@@ -73,6 +73,7 @@ Layout layout_of(int T, int H, int I, int E, int topk)
     L.act = take(max_slots * (size_t)I * sizeof(uint16_t));
     L.actbias = take(max_slots * (size_t)(I / kMinGroup) * sizeof(float));
     L.outf32 = take((size_t)T * H * sizeof(float));
+    L.ccounts = take((size_t)wna16::align_chunks((long long)P) * (E + 1) * sizeof(int32_t));
     L.total = o;
     return L;
 }
@@ -252,6 +253,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.act = reinterpret_cast<uint16_t *>(base + L.act);
     ws.act_bias = reinterpret_cast<float *>(base + L.actbias);
     ws.out_f32 = reinterpret_cast<float *>(base + L.outf32);
+    ws.chunk_counts = reinterpret_cast<int32_t *>(base + L.ccounts);
 
     wna16::KernelEvents ev[4];
     if (events)

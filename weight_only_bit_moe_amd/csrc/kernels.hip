@@ -60,17 +60,22 @@ __device__ __forceinline__ uint32_t bf16_scaled(uint32_t h, int e)
 }
 
 // ---------------------------------------------------------------------------
-// Stable expert sort of the pairs, one workgroup of 1024 threads.
+// Stable expert sort of the pairs, on one or more workgroups of 1024 threads.
 //
-// Pairs are taken in chunks of 1024 in index order.  Inside a chunk a pair's
-// rank among equal experts = (equal experts in earlier waves of the chunk) +
-// (equal experts in earlier lanes of its wave); the lane part comes from 11
-// ballots (one per bit of the expert id), the wave part from a per-wave,
-// per-expert count table in LDS.  A running per-expert fill carries the order
-// across chunks, so the result equals a stable counting sort.
+// Workgroup w places the pairs [w*kAlignChunk, (w+1)*kAlignChunk).  Every
+// workgroup first counts all pairs per expert (the padded exclusive scan of
+// those counts gives the expert offsets) and, separately, the pairs before
+// its own range; its pairs of expert e then start at offset[e] + (pairs of e
+// before the range).  Inside the range, pairs are taken 1024 at a time in
+// index order: a pair's rank among equal experts = (equal experts in earlier
+// waves of the step) + (equal experts in earlier lanes of its wave).  The
+// lane part comes from 11 ballots (one per bit of the expert id), the wave
+// part from a per-wave, per-expert count table in LDS.  The result equals a
+// stable counting sort whatever the number of workgroups.
 // ---------------------------------------------------------------------------
 struct AlignShared {
     int cnt[kMaxExperts];
+    int pre[kMaxExperts];
     int off[kMaxExperts + 1];
     int run[kMaxExperts];
     int wsum[kAlignThreads / 64];
@@ -78,28 +83,71 @@ struct AlignShared {
     uint8_t wcnt[kAlignThreads / 64][kMaxExperts];
 };
 
+// Lanes of the wave holding the same 11-bit key as this lane.
+__device__ __forceinline__ uint64_t match_key(int key)
+{
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) {
+        const uint64_t bb = __ballot((key >> bit) & 1);
+        m &= ((key >> bit) & 1) ? bb : ~bb;
+    }
+    return m;
+}
+
 __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, int P, int E,
                             int bm, int32_t *__restrict__ sorted_ids,
                             int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
                             int32_t *__restrict__ inv_perm, int32_t *__restrict__ num_tiles,
-                            int32_t *__restrict__ bad_ids)
+                            int32_t *__restrict__ bad_ids, int blk, int nblk,
+                            const int32_t *__restrict__ chunk_counts = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int NW = kAlignThreads / 64;
+    const int begin = blk * kAlignChunk;
+    const int end = min(P, begin + kAlignChunk);
     for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
         sh.cnt[e] = 0;
-        sh.run[e] = 0;
+        sh.pre[e] = 0;
         for (int w = 0; w < NW; ++w)
             sh.wcnt[w][e] = 0;
     }
     if (tid == 0)
         sh.bad = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += kAlignThreads) {
-        const int e = ids[p];
-        if (e >= 0 && e < E)
-            atomicAdd(&sh.cnt[e], 1);
-        else
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (chunk_counts != nullptr) {
+        // counts of all pairs and of the pairs before this range, from the
+        // per-chunk counts
+        for (int e = tid; e <= E; e += kAlignThreads) {
+            int all = 0, before = 0;
+            for (int b = 0; b < nblk; ++b) {
+                const int c = chunk_counts[(size_t)b * (E + 1) + e];
+                all += c;
+                before += b < blk ? c : 0;
+            }
+            if (e < E) {
+                sh.cnt[e] = all;
+                sh.pre[e] = before;
+            } else {
+                sh.bad = all;
+            }
+        }
+    }
+    // counts of all pairs and of the pairs before this workgroup's range;
+    // one atomic per distinct expert of each wave
+    for (int base = 0; chunk_counts == nullptr && base < P; base += kAlignThreads) {
+        const int p = base + tid;
+        const int e = p < P ? ids[p] : -1;
+        const bool ok = p < P && e >= 0 && e < E;
+        const uint64_t m = match_key(ok ? e : kMaxExperts);
+        if (ok && (m & below) == 0) {
+            const int c = __popcll(m);
+            atomicAdd(&sh.cnt[e], c);
+            if (base < begin)   // ranges start on multiples of kAlignThreads
+                atomicAdd(&sh.pre[e], c);
+        }
+        if (!ok && p < P)
             atomicAdd(&sh.bad, 1);
     }
     __syncthreads();
@@ -126,18 +174,23 @@ __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, in
         sh.off[E] = acc;
     }
     __syncthreads();
-    if (tid < E)
+    if (tid < E) {
         sh.off[tid] = sh.wsum[wave] + incl - padded;
+        sh.run[tid] = sh.off[tid] + sh.pre[tid];
+    }
     __syncthreads();
     const int total = sh.off[E];
-    for (int e = tid; e <= E; e += kAlignThreads)
-        offsets[e] = sh.off[e];
-    if (tid == 0) {
-        *num_tiles = total / bm;
-        *bad_ids = sh.bad;
+    if (blk == 0) {
+        for (int e = tid; e <= E; e += kAlignThreads)
+            offsets[e] = sh.off[e];
+        if (tid == 0) {
+            *num_tiles = total / bm;
+            *bad_ids = sh.bad;
+        }
     }
-    // tile experts and padding slots
-    for (int s = tid; s < total; s += kAlignThreads) {
+    // tile experts and padding slots: this workgroup's share of the slots
+    const int share = (total + nblk - 1) / nblk;
+    for (int s = blk * share + tid; s < min(total, (blk + 1) * share); s += kAlignThreads) {
         int lo = 0, hi = E - 1;  // last e with off[e] <= s
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -151,19 +204,12 @@ __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, in
         if (s - sh.off[lo] >= sh.cnt[lo])
             sorted_ids[s] = P;
     }
-    // stable placement
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < P; base += kAlignThreads) {
+    // stable placement of this workgroup's pairs
+    for (int base = begin; base < end; base += kAlignThreads) {
         const int p = base + tid;
-        const int e = p < P ? ids[p] : -1;
-        const bool ok = p < P && e >= 0 && e < E;
-        const int key = ok ? e : kMaxExperts;  // 11-bit key; invalid lanes share one key
-        uint64_t m = ~0ull;
-#pragma unroll
-        for (int bit = 0; bit < 11; ++bit) {
-            const uint64_t bb = __ballot((key >> bit) & 1);
-            m &= ((key >> bit) & 1) ? bb : ~bb;
-        }
+        const int e = p < end ? ids[p] : -1;
+        const bool ok = p < end && e >= 0 && e < E;
+        const uint64_t m = match_key(ok ? e : kMaxExperts);  // invalid lanes share one key
         const int rank = __popcll(m & below);
         const bool leader = (m & below) == 0;
         const int cw = __popcll(m);
@@ -174,10 +220,10 @@ __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, in
             int before = 0;
             for (int w = 0; w < wave; ++w)
                 before += sh.wcnt[w][e];
-            const int slot = sh.off[e] + sh.run[e] + before + rank;
+            const int slot = sh.run[e] + before + rank;
             sorted_ids[slot] = p;
             inv_perm[p] = slot;
-        } else if (p < P) {
+        } else if (p < end) {
             inv_perm[p] = -1;
         }
         __syncthreads();
@@ -197,28 +243,56 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 {
     __shared__ AlignShared sh;
     align_block(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
-                bad_ids);
+                bad_ids, blockIdx.x, gridDim.x);
+}
+
+// From this many sort workgroups on, the route kernel's sort takes its
+// counts from align_count_kernel instead of recounting every pair.
+constexpr int kCountedSortBlocks = 8;
+
+// Workgroups the sort of P pairs runs on.
+inline int align_blocks(int P) { return align_chunks(P); }
+
+// Per-chunk expert counts (and invalid ids, in entry E) for the multi-
+// workgroup sort inside the route kernel.
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
+    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ counts)
+{
+    __shared__ int hist[kMaxExperts + 1];
+    for (int e = threadIdx.x; e <= E; e += kAlignThreads)
+        hist[e] = 0;
+    __syncthreads();
+    const int begin = blockIdx.x * kAlignChunk, end = min(P, begin + kAlignChunk);
+    for (int p = begin + threadIdx.x; p < end; p += kAlignThreads) {
+        const int e = ids[p];
+        atomicAdd(&hist[(e >= 0 && e < E) ? e : E], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += kAlignThreads)
+        counts[(size_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
 // ---------------------------------------------------------------------------
-// Route kernel: block 0 sorts the pairs; blocks [1, 1 + nprep) reorder x into
-// fragment order and compute c * (group sum) per (token, w13 group); the
-// remaining blocks zero the FP32 accumulator.
+// Route kernel: blocks [0, nalign) sort the pairs; blocks [nalign, nalign +
+// nprep) reorder x into fragment order and compute c * (group sum) per
+// (token, w13 group); the remaining blocks zero the FP32 accumulator.
 // ---------------------------------------------------------------------------
 template <int BITS, int GS>
 __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int T, int H, int topk,
-    int E, int bm, int nprep, size_t act_bias_n, Workspace ws)
+    int E, int bm, int nalign, int nprep, size_t act_bias_n, Workspace ws)
 {
     __shared__ AlignShared sh;
-    if (blockIdx.x == 0) {
+    const int blk = blockIdx.x;
+    if (blk < nalign) {
         align_block(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert, ws.expert_offsets,
-                    ws.inv_perm, ws.meta, ws.meta + 1);
+                    ws.inv_perm, ws.meta, ws.meta + 1, blk, nalign,
+                    nalign >= kCountedSortBlocks ? ws.chunk_counts : nullptr);
         return;
     }
-    if ((int)blockIdx.x <= nprep) {
+    if (blk < nalign + nprep) {
         const int ngroups = H / GS;
-        const int gid = (blockIdx.x - 1) * kAlignThreads + threadIdx.x;
+        const int gid = (blk - nalign) * kAlignThreads + threadIdx.x;
         if (gid >= T * ngroups)
             return;
         const int t = gid / ngroups, G = gid % ngroups;
@@ -256,8 +330,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     }
     // zero the accumulator and the act bias terms (the decode epilogue adds into them)
     const size_t n4 = (size_t)T * H / 4;
-    const size_t nzero_threads = (size_t)(gridDim.x - 1 - nprep) * kAlignThreads;
-    const size_t first = (size_t)(blockIdx.x - 1 - nprep) * kAlignThreads + threadIdx.x;
+    const size_t nzero_threads = (size_t)(gridDim.x - nalign - nprep) * kAlignThreads;
+    const size_t first = (size_t)(blk - nalign - nprep) * kAlignThreads + threadIdx.x;
     f32x4_t *o = reinterpret_cast<f32x4_t *>(ws.out_f32);
     for (size_t i = first; i < n4; i += nzero_threads)
         o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1349,7 +1423,8 @@ hipError_t launch_align(const int32_t *topk_ids, int T, int topk, int E, int blo
                         int32_t *inv_perm, int32_t *num_tiles, int32_t *bad_ids,
                         hipStream_t stream)
 {
-    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids,
+    hipLaunchKernelGGL(align_kernel, dim3(align_blocks(T * topk)), dim3(kAlignThreads), 0, stream,
+                       topk_ids,
                        T * topk, E, block_m, sorted_ids, tile_expert, expert_offsets, inv_perm,
                        num_tiles, bad_ids);
     return hipGetLastError();
@@ -1367,9 +1442,19 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
         nzero = 1;
     if (nzero > 1024)
         nzero = 1024;
-    hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(1 + nprep + (int)nzero),
-                          dim3(kAlignThreads), 0, stream, ev.start, ev.stop, 0, x, ids, d.T, d.H,
-                          d.topk, d.E, d.block_m, nprep,
+    const int nalign = align_blocks(d.T * d.topk);
+    // With many sort workgroups, each one recounting every pair costs more
+    // than one extra launch: count per chunk first, the sort sums the counts.
+    const bool counted = nalign >= kCountedSortBlocks;
+    hipEvent_t route_start = ev.start;
+    if (counted) {
+        hipExtLaunchKernelGGL(align_count_kernel, dim3(nalign), dim3(kAlignThreads), 0, stream,
+                              ev.start, nullptr, 0, ids, d.T * d.topk, d.E, ws.chunk_counts);
+        route_start = nullptr;
+    }
+    hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(nalign + nprep + (int)nzero),
+                          dim3(kAlignThreads), 0, stream, route_start, ev.stop, 0, x, ids, d.T, d.H,
+                          d.topk, d.E, d.block_m, nalign, nprep,
                           // only the decode-shaped w13 adds into act_bias
                           d.variant13 == 2 ? (size_t)d.max_tiles * d.block_m * (d.I / d.g2) : 0,
                           ws);

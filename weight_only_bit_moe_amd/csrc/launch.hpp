@@ -20,7 +20,12 @@ struct Workspace {
     uint16_t *act;            // [max_slots, I] bf16, fragment order per w2 group
     float *act_bias;          // [max_slots, I / g2]
     float *out_f32;           // [T, H]
+    int32_t *chunk_counts;    // [align chunks][E + 1]: per-chunk expert counts, then invalid ids
 };
+
+// Pairs per workgroup of the expert sort.
+constexpr int kAlignChunk = 4096;
+inline int align_chunks(long long P) { return P <= kAlignChunk ? 1 : (int)((P + kAlignChunk - 1) / kAlignChunk); }
 
 // Optional start/stop events recorded by the kernel dispatch itself
 // (hipExtLaunchKernelGGL); null events record nothing.
