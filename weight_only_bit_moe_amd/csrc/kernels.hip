@@ -1172,6 +1172,20 @@ struct Stream {
         }
     }
 
+    // Negated bias term of LDS item i ([group][row], then 4 zeros): the start
+    // of each MFMA chain.
+    static constexpr int NBIAS_PRE = 2;
+    static __device__ __forceinline__ float bias_item(const GemmArgs &args, int s0, int s1, int s2,
+                                                      int s3, int i, int ngroups)
+    {
+        static_assert(R == 4, "four tile rows");
+        const int G = i / R, r = i % R;
+        int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
+        sr = i < R * ngroups ? sr : -1;
+        const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups + (G < ngroups ? G : 0)];
+        return sr >= 0 ? -bv : 0.f;
+    }
+
     static __device__ void run(const GemmArgs &args)
     {
         extern __shared__ __align__(16) unsigned char smem[];
@@ -1227,7 +1241,15 @@ struct Stream {
 
         // Activation rows (zero for padding rows), their bias terms and this
         // workgroup's scales go to LDS.  Each pass issues all of its loads
-        // before its first LDS store, so the latencies overlap.
+        // before its first LDS store, so the latencies overlap; the first bias
+        // items load together with the first pass.
+        float bpre[NBIAS_PRE];
+#pragma unroll
+        for (int k = 0; k < NBIAS_PRE; ++k) {
+            const int i = tid + k * NTHREADS;
+            bpre[k] = i < R * ngroups + 4 ? bias_item(args, src[0], src[1], src[2], src[3], i, ngroups)
+                                          : 0.f;
+        }
         {
             const int k8n = K / 8;
             const int srows = NW * NB * 16;
@@ -1276,16 +1298,14 @@ struct Stream {
                 }
             }
             for (int i = tid; i < R * ngroups + 4; i += NTHREADS) {
-                const int G = i / R, r = i % R;   // [group][row]; the last 4 stay zero
-                int sr = src[0];
-#pragma unroll
-                for (int rr = 1; rr < R; ++rr)
-                    sr = r == rr ? src[rr] : sr;
-                sr = i < R * ngroups ? sr : -1;
-                const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups +
-                                             (G < ngroups ? G : 0)];
-                sBias[i] = sr >= 0 ? -bv : 0.f;  // negated: the start of each MFMA chain
+                if (i < NBIAS_PRE * NTHREADS)
+                    continue;   // staged from the batch loaded above
+                sBias[i] = bias_item(args, src[0], src[1], src[2], src[3], i, ngroups);
             }
+#pragma unroll
+            for (int k = 0; k < NBIAS_PRE; ++k)
+                if (tid + k * NTHREADS < R * ngroups + 4)
+                    sBias[tid + k * NTHREADS] = bpre[k];
             if (!svec) {   // scales without 16-byte alignment: one half at a time
                 for (int i = tid; i < srows * ngroups; i += NTHREADS) {
                     const int rr = i / ngroups, G = i % ngroups;
