@@ -5,13 +5,15 @@
 //            expert-contiguous tiles of block_m rows; other blocks: copy x into
 //            MFMA fragment order with a per-group bias term, and zero the FP32
 //            accumulator.
-//   w13      per (tile, 128 gate columns): gather the tile's token rows, stream
-//            packed codes straight from HBM into registers, unpack to biased
-//            BF16, 16x16x32 BF16 MFMA per K group, scale each group's partial
-//            product once in FP32, SwiGLU(alpha, beta, clamp) epilogue -> BF16
-//            act in fragment order plus its per-group bias term.
-//   w2       per (tile, 128 output columns): same GEMM over act; the epilogue
-//            adds routing_weight * y into out_f32 with FP32 atomics.
+//   w13      per (tile, column block): decode-shaped 4-row tiles stream packed
+//            codes straight from HBM into registers; prefill-shaped 64-row
+//            tiles copy every operand into an LDS ring.  Both unpack codes to
+//            biased BF16, run 16x16x32 BF16 MFMA chains per K group, scale each
+//            group's partial product once in FP32, and end in a
+//            SwiGLU(alpha, beta, clamp) epilogue -> BF16 act in fragment order
+//            plus its per-group bias term.
+//   w2       per (tile, column block): same GEMM over act; the epilogue adds
+//            routing_weight * y into out_f32 with FP32 atomics.
 //   convert  out_f32 -> BF16 (round to nearest even).
 //
 // Weight format (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
 
 // ---------------------------------------------------------------------------
 // Route kernel: blocks [0, nalign) sort the pairs; blocks [nalign, nalign +
-// nprep) reorder x into fragment order and compute c * (group sum) per
+// nprep) reorder x into fragment order and compute minus c * (group sum) per
 // (token, w13 group); the remaining blocks zero the FP32 accumulator.
 // ---------------------------------------------------------------------------
 template <int BITS, int GS>
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
             }
             dst[q] = o;
         }
-        ws.x_bias[(size_t)t * ngroups + G] = sum;
+        ws.x_bias[(size_t)t * ngroups + G] = -sum;   // stored negated: the chain start
         return;
     }
     // zero the accumulator and the act bias terms (the decode epilogue adds into them)
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
 // ---------------------------------------------------------------------------
 struct GemmArgs {
     const uint16_t *a;        // W13: x_perm [T][K]; W2: act [slots][K]
-    const float *a_bias;      // W13: x_bias [T][K/gs]; W2: act_bias [slots][K/gs]
+    const float *a_bias;      // negated bias terms; W13: x_bias [T][K/gs]; W2: act_bias [slots][K/gs]
     const uint32_t *codes;    // [E][rows][K*bits/32]
     const uint16_t *scales;   // [E][rows][K/gs]
     const int32_t *sorted_ids;
@@ -464,24 +466,33 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
 // ---------------------------------------------------------------------------
 // Prefill-shaped grouped WNA16 GEMM ("tile" kernel).
 //
-// Workgroup = 4 waves on one tile of up to 64 (token, slot) rows of one
-// expert and 256 weight rows (w13: 128 gate rows and the 128 matching up
-// rows; w2: 256 output columns).  The waves split the weight rows (64 each,
+// Workgroup = 8 waves on one tile of up to 64 (token, slot) rows of one
+// expert and 512 weight rows (w13: 256 gate rows and the 256 matching up
+// rows; w2: 512 output columns).  The waves split the weight rows (64 each,
 // four 16-column subtiles), so every wave multiplies all of the tile's row
-// subtiles: each unpacked code fragment feeds up to 4 MFMAs and each
-// activation fragment 4.  Row subtiles beyond the tile's real rows are
-// skipped, so a 5-row expert costs one subtile, not four.
+// subtiles: each unpacked code fragment feeds up to 4 MFMAs.  Row subtiles
+// beyond the tile's real rows are skipped, so a 5-row expert costs one
+// subtile, not four.
 //
 // K runs in chunks of 128.  Every operand of a chunk -- activation rows
-// (already in fragment order), their bias terms, codes and scales -- is
+// (already in fragment order), codes, scales and the rows' bias terms -- is
 // copied from memory straight into LDS (global_load_lds, no registers) in
-// the order the MFMA lanes read it, so each read is one conflict-free
-// ds_read.  The copies run 1-2 chunks ahead through a ring of LDS stages,
-// with one barrier per chunk and explicit vmcnt waits.
+// the order the MFMA lanes read it, so each read is one ds_read.  The copies
+// run 2-3 chunks ahead through a ring of LDS stages with explicit vmcnt
+// waits.
+//
+// Work per chunk and wave has two halves: a VALU half that reads the
+// chunk's codes and unpacks them to BF16 fragments, and an MFMA half that
+// runs the chains (and folds each group's chain into the FP32 accumulators
+// with its scale).  Waves 0-3 and 4-7 -- one of each on every SIMD -- run
+// the halves in alternation, half a chunk apart, so that on every SIMD one
+// wave issues MFMAs while the other keeps the VALU busy; a barrier between
+// halves keeps the two groups in step, and the MFMA half runs at a raised
+// wave priority.
 //
 // Workgroup ids are spread over the 8 XCDs round-robin by the hardware; the
 // kernel gives each XCD a contiguous run of (tile, column block) items,
-// tile-major, so one XCD's L2 serves both the 16 column blocks of a tile
+// tile-major, so one XCD's L2 serves both the column blocks of a tile
 // (activation reuse) and consecutive tiles of one expert (weight reuse).
 // ---------------------------------------------------------------------------
 // LDS address (byte offset in the workgroup's LDS) of a __shared__ pointer.
@@ -534,36 +545,38 @@ struct Tile {
     static constexpr int BN = NW * NT * 16;          // weight rows per workgroup (512)
     static constexpr int OUTC = W13 ? BN / 2 : BN;   // output columns per workgroup
     static constexpr int KC = 128;                   // K per chunk
+    static constexpr int KS = KC / 32;               // MFMA steps per chunk
     static constexpr int GPC = KC / GS;              // groups per chunk
     static constexpr int S = GS / 32;                // MFMA steps per group
     static constexpr int NDW = CodeTraits<BITS, GS>::NDW;
     static constexpr int RB = KC * BITS / 8;         // code bytes of one row per chunk
     static constexpr int PIECES = RB / 16;           // 16-byte pieces per row and chunk
-    static constexpr int SEGG = 32;                  // groups per scale/bias segment
     static constexpr int ACT_STRIDE = OUTC + 8;      // W13 epilogue tile, bf16 elements
     static constexpr int kXcds = 8;
 
-    // LDS:
-    //   scales [group in segment][wave][column][subtile] halves         32 KB
-    //   bias   [group in segment][row] floats, negated                   8 KB
-    //   ring of STAGES stages, each
-    //     A     [subtile][step][lane] 16-byte MFMA fragments            16 KB
-    //     codes [wave][subtile row][RB bytes], 16-byte pieces swizzled  NW*64*RB
-    static constexpr int SC_BYTES = SEGG * NW * 64 * 2;
-    static constexpr int BI_OFF = SC_BYTES;
-    static constexpr int RING_OFF = BI_OFF + SEGG * BM * 4;
+    // LDS: a ring of STAGES stages, each holding one chunk:
+    //   A      [subtile][step][lane] 16-byte MFMA fragments              16 KB
+    //   codes  [wave][subtile row][RB bytes], 16-byte pieces swizzled    NW*64*RB
+    //   scales [wave][group][lane] dword slots, FP16 in the low half,
+    //          lane = column * 4 + subtile                                NW*GPC*256
+    //   bias   [group][row] FP32 (the chain start: minus the bias term)  GPC*256
     static constexpr int A_OFF = 0;
-    static constexpr int B_OFF = MT * 4 * 64 * 16;
+    static constexpr int B_OFF = MT * KS * 64 * 16;
     static constexpr int B_WAVE = 64 * RB;
-    static constexpr int STAGE = B_OFF + NW * B_WAVE;
-    static constexpr int STAGES = RING_OFF + 3 * STAGE <= 150 * 1024 ? 3 : 2;
-    static constexpr int LDS_BYTES = RING_OFF + STAGES * STAGE;
+    static constexpr int SC_OFF = B_OFF + NW * B_WAVE;
+    static constexpr int SC_WAVE = GPC * 64 * 4;
+    static constexpr int BI_OFF = SC_OFF + NW * SC_WAVE;
+    static constexpr int STAGE = BI_OFF + GPC * 64 * 4;
+    static constexpr int kLdsBudget = 160 * 1024 - 1024;   // the rest holds the row table
+    static constexpr int STAGES = kLdsBudget / STAGE >= 4 ? 4 : kLdsBudget / STAGE;
+    static_assert(STAGES >= 2, "two chunks must fit in LDS");
+    static constexpr int LDS_BYTES = STAGES * STAGE;
 
     struct EpiW13 {
         uint16_t act[BM * ACT_STRIDE];
         float part[BM * (OUTC / 8)];
     };
-    static_assert(sizeof(EpiW13) <= STAGES * STAGE, "epilogue tile overlays the ring");
+    static_assert(sizeof(EpiW13) <= LDS_BYTES, "epilogue tile overlays the ring");
     struct Rows {
         int pair[BM];
         int src[BM];
@@ -579,9 +592,12 @@ struct Tile {
     struct Ctx {
         const uint16_t *a;
         const uint32_t *codes;      // this expert's codes
-        uint32_t aoff[2];           // activation rows of the A pieces this lane copies
-        uint32_t akoff[2];          // their K offset inside a chunk (bytes)
+        const uint16_t *scales;     // this expert's scales
+        const float *bias;          // bias terms of the A rows
+        uint32_t aoff[2];           // A pieces this lane copies: row and K offset (bytes)
         uint32_t coff[4];           // code rows this lane copies (byte offsets)
+        uint32_t soff;              // scale row this lane copies (byte offset)
+        uint32_t boff;              // bias row this lane copies (byte offset)
         uint32_t ring;              // LDS address of the ring
         int b, nb, col0, tid, lane, wave, g;
         bool wave_on;
@@ -599,13 +615,14 @@ struct Tile {
         __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
     }
 
-    // A pieces each wave copies per chunk (16 slots shared by 8 waves; slots of
-    // inactive subtiles get harmless copies so every wave issues the same number)
+    // Copies each wave issues per chunk: A pieces (16 slots shared by 8
+    // waves; slots of inactive subtiles get harmless copies so every wave
+    // issues the same number), its code pieces, its scales (one 2-byte copy
+    // per group) and, for waves below GPC, the bias terms of group `wave`.
     template <int MTA>
     static constexpr int a_copies() { return MTA <= 2 ? 1 : 2; }
-    static constexpr int code_copies() { return 64 * PIECES / 64; }   // = PIECES
     template <int MTA>
-    static constexpr int copies() { return a_copies<MTA>() + code_copies(); }
+    static constexpr int copies() { return a_copies<MTA>() + PIECES + GPC; }
 
     template <int MTA>
     static __device__ __forceinline__ void issue(int stage, const Ctx &cx, int kc)
@@ -614,31 +631,56 @@ struct Tile {
 #pragma unroll
         for (int k = 0; k < a_copies<MTA>(); ++k) {
             const int slot = cx.wave + NW * k;   // [subtile][step]
-            copy_to_lds<16>(cx.a, cx.aoff[k] + cx.akoff[k] + (uint32_t)kc * (KC * 2),
+            copy_to_lds<16>(cx.a, cx.aoff[k] + (uint32_t)kc * (KC * 2),
                             st + A_OFF + slot * 64 * 16);
         }
         const uint32_t bw = st + B_OFF + cx.wave * B_WAVE;
 #pragma unroll
-        for (int k = 0; k < code_copies(); ++k)
+        for (int k = 0; k < PIECES; ++k)
             copy_to_lds<16>(cx.codes, cx.coff[k] + (uint32_t)kc * RB, bw + k * 64 * 16);
+#pragma unroll
+        for (int G = 0; G < GPC; ++G)
+            copy_to_lds<2>(cx.scales, cx.soff + (uint32_t)(kc * GPC + G) * 2u,
+                           st + SC_OFF + (cx.wave * GPC + G) * 256);
+        if (cx.wave < GPC)
+            copy_to_lds<4>(cx.bias, cx.boff + (uint32_t)(kc * GPC + cx.wave) * 4u,
+                           st + BI_OFF + cx.wave * 256);
     }
 
-    template <int MTA>
-    static __device__ __forceinline__ void compute(const unsigned char *lds, int stage, int kc,
-                                                   int seg_g0, const Ctx &cx,
-                                                   f32x4_t (&acc)[MTA][NT],
-                                                   const UnpackConsts &magic)
+    // Wait until this wave's copies of the chunk with `after` later chunks
+    // already issued have landed.
+    template <int L>
+    static __device__ __forceinline__ void wait_chunk_l(int after)
     {
-        const int lane = cx.lane, g = cx.g, c = lane & 15;
-        const unsigned char *st = lds + RING_OFF + stage * STAGE;
-        const unsigned char *bw = st + B_OFF + cx.wave * B_WAVE;
+        if (after >= 3)
+            wait_vm<3 * L>();
+        else if (after == 2)
+            wait_vm<2 * L>();
+        else if (after == 1)
+            wait_vm<L>();
+        else
+            wait_vm<0>();
+    }
+    template <int MTA>
+    static __device__ __forceinline__ void wait_chunk(const Ctx &cx, int after)
+    {
+        static_assert(3 * (copies<MTA>() + 1) < 64, "copies in flight exceed the wait counter");
+        if (cx.wave < GPC)
+            wait_chunk_l<copies<MTA>() + 1>(after);
+        else
+            wait_chunk_l<copies<MTA>()>(after);
+    }
+
+    // VALU half: the chunk's codes of this wave's rows, unpacked into the
+    // B fragments of all KS steps.
+    static __device__ __forceinline__ void unpack_chunk(const unsigned char *lds, int stage,
+                                                        const Ctx &cx, bf16x8_t (&bf)[NT][KS],
+                                                        const UnpackConsts &magic)
+    {
+        const int g = cx.g, c = cx.lane & 15;
+        const unsigned char *bw = lds + stage * STAGE + B_OFF + cx.wave * B_WAVE;
 #pragma unroll
         for (int G = 0; G < GPC; ++G) {
-            const int Gs = kc * GPC + G - seg_g0;   // group inside the segment
-            bf16x8_t bf[NT][S];
-            float sc[NT];
-            const u32x2_t sp =
-                *reinterpret_cast<const u32x2_t *>(lds + ((Gs * NW + cx.wave) * 64 + c * 4) * 2);
             const int off = CodeTraits<BITS, GS>::dword_off(G, g) * 4;   // inside the row's chunk
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
@@ -661,124 +703,105 @@ struct Tile {
                 }
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    bf[j][s] = unpack<BITS, GS, NDW>(q, s, g, magic);
-                sc[j] = f16_to_f32((uint16_t)(sp[j >> 1] >> (16 * (j & 1))));
+                    bf[j][G * S + s] = unpack<BITS, GS, NDW>(q, s, g, magic);
             }
+        }
+    }
+
+    // MFMA half: for each active row subtile and group, one chain per column
+    // subtile starting from minus the bias term, folded into the
+    // accumulators with the group's scale.  The next subtile's activation
+    // fragments (and, for groups of 64 or more, bias terms) are read while
+    // the current one's MFMAs run, and the last fold of a subtile runs under
+    // the next subtile's MFMAs.
+    static constexpr bool PRE_BIAS = GPC <= 2;
+    template <int MTA>
+    static __device__ __forceinline__ void mfma_chunk(const unsigned char *lds, int stage,
+                                                      const Ctx &cx, const bf16x8_t (&bf)[NT][KS],
+                                                      f32x4_t (&acc)[MTA][NT])
+    {
+        const int lane = cx.lane, g = cx.g, c = lane & 15;
+        const unsigned char *st = lds + stage * STAGE;
+        auto scales = [&](int G) {
+            return *reinterpret_cast<const u32x4_t *>(
+                st + SC_OFF + ((cx.wave * GPC + G) * 64 + c * 4) * 4);
+        };
+        auto bias = [&](int i, int G) {
+            return *reinterpret_cast<const f32x4_t *>(st + BI_OFF + (G * 64 + i * 16 + 4 * g) * 4);
+        };
+        bf16x8_t af[KS];
+        f32x4_t nb[GPC];
 #pragma unroll
-            for (int i = 0; i < MTA; ++i) {
-                bf16x8_t af[S];
+        for (int s = 0; s < KS; ++s)
+            af[s] = *reinterpret_cast<const bf16x8_t *>(st + A_OFF + (s * 64 + lane) * 16);
+        if constexpr (PRE_BIAS) {
 #pragma unroll
-                for (int s = 0; s < S; ++s)
-                    af[s] = *reinterpret_cast<const bf16x8_t *>(
-                        st + A_OFF + ((i * 4 + G * S + s) * 64 + lane) * 16);
-                const f32x4_t nb = *reinterpret_cast<const f32x4_t *>(
-                    lds + BI_OFF + (Gs * BM + i * 16 + 4 * g) * 4);
+            for (int G = 0; G < GPC; ++G)
+                nb[G] = bias(0, G);
+        }
+        f32x4_t pend[NT];   // last chain of the previous subtile, not yet folded
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) {
+            bf16x8_t an[KS];
+            f32x4_t nbn[GPC];
+            if (i + 1 < MTA) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    an[s] = *reinterpret_cast<const bf16x8_t *>(
+                        st + A_OFF + (((i + 1) * KS + s) * 64 + lane) * 16);
+                if constexpr (PRE_BIAS) {
+#pragma unroll
+                    for (int G = 0; G < GPC; ++G)
+                        nbn[G] = bias(i + 1, G);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int G = 0; G < GPC; ++G) {
+                if constexpr (!PRE_BIAS)
+                    nb[G] = bias(i, G);
                 f32x4_t accg[NT];
 #pragma unroll
                 for (int s = 0; s < S; ++s)
 #pragma unroll
                     for (int j = 0; j < NT; ++j)
                         accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            af[s], bf[j][s], s == 0 ? nb : accg[j], 0, 0, 0);
+                            af[G * S + s], bf[j][G * S + s], s == 0 ? nb[G] : accg[j], 0, 0, 0);
+                if (G == 0 && i > 0)
+                    fold(acc[i - 1], pend, scales(GPC - 1));
+                if (G + 1 < GPC) {
+                    fold(acc[i], accg, scales(G));
+                } else {
 #pragma unroll
-                for (int j = 0; j < NT; ++j)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[i][j][v] = fmaf(sc[j], accg[j][v], acc[i][j][v]);
-            }
-        }
-    }
-
-    // Scales of the workgroup's weight rows and negated bias terms of the
-    // tile's rows for groups [g0, g0 + ng) go to LDS.  Plain loads, issued
-    // in batches so their latencies overlap; this runs once per segment
-    // (normally once per workgroup).
-    static __device__ __forceinline__ int wg_row(const GemmArgs &args, int nb, int q, bool &valid)
-    {
-        // q = workgroup weight row in [wave][column][subtile] order
-        const int w = q >> 6, cc = (q >> 2) & 15, j = q & 3;
-        if constexpr (W13) {
-            const int col = nb * OUTC + w * 32 + (j & 1) * 16 + cc;
-            valid = col < args.N;
-            return args.N * (j >> 1) + col;
-        } else {
-            const int n = nb * OUTC + w * 64 + j * 16 + cc;
-            valid = n < args.N;
-            return n;
-        }
-    }
-
-    static __device__ __forceinline__ void load_segment(unsigned char *lds, const Rows &rows,
-                                                        const GemmArgs &args, const Ctx &cx,
-                                                        int e, int g0, int ng)
-    {
-        const int K = args.K, ngroups = K / GS;
-        const int nrows = W13 ? 2 * args.N : args.N;
-        const uint16_t *sbase = args.scales + (size_t)e * nrows * ngroups;
-        uint16_t *sc = reinterpret_cast<uint16_t *>(lds);
-        float *bi = reinterpret_cast<float *>(lds + BI_OFF);
-        const bool vec = ng == SEGG && ngroups % 8 == 0 && g0 % 8 == 0 &&
-                         reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
-        if (vec) {
-            // 16-byte pieces: 8 groups of one weight row; 512 rows x 4 pieces
-            constexpr int PER = BN * (SEGG / 8) / NTHREADS;
-            u32x4_t v[PER];
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int idx = cx.tid + k * NTHREADS;
-                const int q = idx / (SEGG / 8), pc = idx % (SEGG / 8);
-                bool valid;
-                const int n = wg_row(args, cx.nb, q, valid);
-                v[k] = valid ? *reinterpret_cast<const u32x4_t *>(
-                                   sbase + (size_t)n * ngroups + g0 + pc * 8)
-                             : u32x4_t{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int idx = cx.tid + k * NTHREADS;
-                const int q = idx / (SEGG / 8), pc = idx % (SEGG / 8);
-#pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    sc[(pc * 8 + h) * BN + q] = (uint16_t)(v[k][h >> 1] >> (16 * (h & 1)));
-            }
-        } else {
-            // any alignment: 8 halves per thread and batch
-            for (int base = 0; base < BN * ng; base += 8 * NTHREADS) {
-                uint16_t h[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int idx = base + cx.tid + k * NTHREADS;
-                    const int q = idx / ng, Gl = idx % ng;
-                    bool valid;
-                    const int n = wg_row(args, cx.nb, q < BN ? q : 0, valid);
-                    h[k] = (idx < BN * ng && valid) ? sbase[(size_t)n * ngroups + g0 + Gl]
-                                                    : (uint16_t)0;
+                    for (int j = 0; j < NT; ++j)
+                        pend[j] = accg[j];
                 }
+            }
+            if (i + 1 < MTA) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int idx = base + cx.tid + k * NTHREADS;
-                    if (idx < BN * ng)
-                        sc[(idx % ng) * BN + idx / ng] = h[k];
+                for (int s = 0; s < KS; ++s)
+                    af[s] = an[s];
+                if constexpr (PRE_BIAS) {
+#pragma unroll
+                    for (int G = 0; G < GPC; ++G)
+                        nb[G] = nbn[G];
                 }
             }
         }
-        // bias terms: 64 rows x ng floats; 4 groups per 16-byte piece when possible
-        if (ng % 4 == 0 && ngroups % 4 == 0 && g0 % 4 == 0) {
-            const int pieces = BM * (ng / 4);   // <= 512
-            const int idx = cx.tid;
-            if (idx < pieces) {
-                const int r = idx / (ng / 4), pc = idx % (ng / 4);
-                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(
-                    args.a_bias + (size_t)rows.src[r] * ngroups + g0 + pc * 4);
+        fold(acc[MTA - 1], pend, scales(GPC - 1));
+    }
+
+    // acc[j] += scale[j] * part[j]; scale j is the FP16 value in the low half
+    // of sv[j]
+    static __device__ __forceinline__ void fold(f32x4_t (&acc)[NT], const f32x4_t (&part)[NT],
+                                                const u32x4_t &sv)
+    {
 #pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    bi[(pc * 4 + h) * BM + r] = -v[h];
-            }
-        } else {
-            for (int idx = cx.tid; idx < BM * ng; idx += NTHREADS) {
-                const int r = idx / ng, Gl = idx % ng;
-                bi[Gl * BM + r] = -args.a_bias[(size_t)rows.src[r] * ngroups + g0 + Gl];
-            }
+        for (int j = 0; j < NT; ++j) {
+            const float sc = f16_to_f32((uint16_t)(sv[j] & 0xffffu));
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[j][v] = fmaf(sc, part[j][v], acc[j][v]);
         }
     }
 
@@ -818,16 +841,18 @@ struct Tile {
                 rows.real = __popcll(m);
         }
         __syncthreads();
-        const int K = args.K;
+        const int K = args.K, ngroups = K / GS;
         cx.a = args.a;
         // A pieces: slot = wave + 8k -> subtile slot / 4, step slot % 4
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int slot = cx.wave + NW * k;
-            cx.aoff[k] = (uint32_t)rows.src[(slot >> 2) * 16 + (lane & 15)] * (uint32_t)K * 2u;
-            cx.akoff[k] = (uint32_t)((slot & 3) * 32 + (lane >> 4) * 8) * 2u;
+            cx.aoff[k] = (uint32_t)rows.src[(slot >> 2) * 16 + (lane & 15)] * (uint32_t)K * 2u +
+                         (uint32_t)((slot & 3) * 32 + (lane >> 4) * 8) * 2u;
         }
-        cx.ring = lds_address(lds + RING_OFF);
+        cx.bias = args.a_bias;
+        cx.boff = (uint32_t)rows.src[lane] * (uint32_t)ngroups * 4u;
+        cx.ring = lds_address(lds);
 
         // weight rows of this wave; a wave past the last column stays idle but
         // keeps copying (valid rows) and taking part in the barriers
@@ -836,40 +861,71 @@ struct Tile {
         cx.wave_on = cx.col0 < args.N;
         const uint32_t kw = (uint32_t)(K * BITS / 32);
         cx.codes = args.codes + (size_t)e * nrows * kw;
+        cx.scales = args.scales + (size_t)e * nrows * ngroups;
+        // weight row of (subtile j, column cc) of this wave
+        auto wrow = [&](int j, int cc) -> uint32_t {
+            if (!cx.wave_on)
+                return 0u;
+            if constexpr (W13)
+                return (uint32_t)(cx.col0 + (j % (NT / 2)) * 16 + cc + (j >= NT / 2 ? args.N : 0));
+            else
+                return (uint32_t)(cx.col0 + j * 16 + cc);
+        };
         // code copy k of this lane: 16-byte slot lane of rows [k*64/PIECES, ...)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int slot = k * 64 + lane;                      // in [row][position]
             const int row = slot / PIECES, pos = slot % PIECES;  // wave-local row j*16 + c
             const int piece = pos ^ swz(row);
-            const int j = row >> 4, cc = row & 15;
-            uint32_t n = 0;
-            if (cx.wave_on && row < 64) {
-                if constexpr (W13)
-                    n = (uint32_t)(cx.col0 + (j % (NT / 2)) * 16 + cc + (j >= NT / 2 ? args.N : 0));
-                else
-                    n = (uint32_t)(cx.col0 + j * 16 + cc);
-            }
+            const uint32_t n = row < 64 ? wrow(row >> 4, row & 15) : 0u;
             cx.coff[k] = n * kw * 4u + (uint32_t)piece * 16u;
         }
+        // scale copies: lane = column * 4 + subtile
+        cx.soff = wrow(lane & 3, lane >> 2) * (uint32_t)ngroups * 2u;
 
         switch ((rows.real + 15) >> 4) {
-        case 1: body<1>(lds, rows, args, cx, e); break;
-        case 2: body<2>(lds, rows, args, cx, e); break;
-        case 3: body<3>(lds, rows, args, cx, e); break;
-        default: body<4>(lds, rows, args, cx, e); break;
+        case 1: body<1>(lds, rows, args, cx); break;
+        case 2: body<2>(lds, rows, args, cx); break;
+        case 3: body<3>(lds, rows, args, cx); break;
+        default: body<4>(lds, rows, args, cx); break;
         }
     }
 
     // The K loop and epilogue for a tile with MTA active 16-row subtiles.
-    // Chunk kc lives in stage kc % STAGES; the copies of chunk kc + STAGES - 1
-    // are issued right after the barrier that ends the reads of chunk kc - 1.
+    //
+    // Phases, separated by workgroup barriers (chunk k lives in stage
+    // k % STAGES):
+    //   phase -1:    waves 0-3 unpack chunk 0
+    //   phase 2k:    waves 0-3 run the MFMAs of chunk k, waves 4-7 unpack it
+    //   phase 2k+1:  waves 0-3 unpack chunk k+1, waves 4-7 run the MFMAs of k
+    // Every wave runs the same sequence (unpack 0, MFMAs 0, unpack 1, ...);
+    // waves 4-7 run it one phase later.  Chunk k is last read in phase
+    // 2k+1, so the copies of chunk k + STAGES go into its stage during phase
+    // 2k+2; chunk k+1 must have landed before the barrier that opens phase
+    // 2k+1.
+    template <int MTA>
+    static __device__ __forceinline__ void open_phase(const Ctx &cx, int p, int nchunks)
+    {
+        if (p & 1) {
+            const int j = (p - 1) >> 1;   // chunk j + 1 is read from this phase on
+            if (j + 1 < nchunks)
+                wait_chunk<MTA>(cx, min(STAGES - 2, nchunks - 2 - j));
+        }
+        workgroup_barrier();
+    }
+    // Copies issued during phase 2j (chunk j - 1 is no longer read): waves
+    // 4-7 issue them before their unpack, waves 0-3 after their MFMAs.
+    template <int MTA>
+    static __device__ __forceinline__ void issue_phase(const Ctx &cx, int j, int nchunks)
+    {
+        if (j >= 1 && j - 1 + STAGES < nchunks)
+            issue<MTA>((j - 1) % STAGES, cx, j - 1 + STAGES);
+    }
+
     template <int MTA>
     static __device__ void body(unsigned char *lds, const Rows &rows, const GemmArgs &args,
-                                const Ctx &cx, int e)
+                                const Ctx &cx)
     {
-        constexpr int L = copies<MTA>();
-        static_assert((STAGES - 1) * L < 64, "copies in flight exceed the wait counter");
         f32x4_t acc[MTA][NT];
 #pragma unroll
         for (int i = 0; i < MTA; ++i)
@@ -879,37 +935,40 @@ struct Tile {
 
         const UnpackConsts magic = unpack_consts();
         const int nchunks = args.K / KC;
-        const int ngroups = args.K / GS;
-        constexpr int SEGC = SEGG / GPC;   // chunks per segment
+        const int late = cx.wave >= 4 ? 1 : 0;   // waves 4-7 run one phase later
+        const bool on = cx.wave_on;
+
 #pragma unroll
-        for (int p = 0; p < STAGES - 1; ++p)
+        for (int p = 0; p < STAGES; ++p)
             if (p < nchunks)
                 issue<MTA>(p, cx, p);
-        for (int kc = 0; kc < nchunks; ++kc) {
-            if (kc % SEGC == 0) {
-                // new scale/bias segment: everyone is done with the previous one
-                workgroup_barrier();
-                const int g0 = kc * GPC;
-                load_segment(lds, rows, args, cx, e, g0, min(SEGG, ngroups - g0));
+        wait_chunk<MTA>(cx, min(STAGES - 1, nchunks - 1));
+        workgroup_barrier();   // opens phase -1
+
+        for (int k = 0; k < nchunks; ++k) {
+            bf16x8_t bf[NT][KS];
+            if (k > 0 || late)
+                open_phase<MTA>(cx, 2 * k - 1 + late, nchunks);
+            if (late)
+                issue_phase<MTA>(cx, k, nchunks);   // phase 2k: before the unpack
+            if (on)
+                unpack_chunk(lds, k % STAGES, cx, bf, magic);
+            open_phase<MTA>(cx, 2 * k + late, nchunks);
+            if (on) {
+                __builtin_amdgcn_s_setprio(1);
+                mfma_chunk<MTA>(lds, k % STAGES, cx, bf, acc);
+                __builtin_amdgcn_s_setprio(0);
             }
-            // this wave's copies of chunk kc have landed (later chunks may not have)
-            if (STAGES == 3 && kc + 1 < nchunks)
-                wait_vm<(STAGES - 2) * L>();
-            else
-                wait_vm<0>();
-            workgroup_barrier();
-            const int nx = kc + STAGES - 1;
-            if (nx < nchunks)
-                issue<MTA>(nx % STAGES, cx, nx);
-            if (cx.wave_on)
-                compute<MTA>(lds, kc % STAGES, kc, (kc / SEGC) * SEGG, cx, acc, magic);
+            if (!late)
+                issue_phase<MTA>(cx, k, nchunks);   // phase 2k: after the MFMAs
         }
+        if (!late)
+            open_phase<MTA>(cx, 2 * nchunks - 1, nchunks);   // waves 0-3 idle in the last phase
         __syncthreads();   // every wave is done with the ring
 
         const int rows_real = rows.real;
         if constexpr (W13) {
-            epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(lds + RING_OFF), args, acc, cx,
-                              rows_real);
+            epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(lds), args, acc, cx, rows_real);
         } else {
             if (!cx.wave_on)
                 return;
@@ -1004,7 +1063,7 @@ struct Tile {
 #pragma unroll
             for (int k = 0; k < per; ++k)
                 sum += epi->part[r * (OUTC / 8) + gl * per + k];
-            args.act_bias_out[(size_t)(cx.b * BM + r) * ngroups2 + cx.nb * (OUTC / G2) + gl] = sum;
+            args.act_bias_out[(size_t)(cx.b * BM + r) * ngroups2 + cx.nb * (OUTC / G2) + gl] = -sum;
         }
     }
 };
@@ -1172,8 +1231,8 @@ struct Stream {
         }
     }
 
-    // Negated bias term of LDS item i ([group][row], then 4 zeros): the start
-    // of each MFMA chain.
+    // Negated bias term (stored negated) of LDS item i ([group][row], then 4
+    // zeros): the start of each MFMA chain.
     static constexpr int NBIAS_PRE = 2;
     static __device__ __forceinline__ float bias_item(const GemmArgs &args, int s0, int s1, int s2,
                                                       int s3, int i, int ngroups)
@@ -1183,7 +1242,7 @@ struct Stream {
         int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
         sr = i < R * ngroups ? sr : -1;
         const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups + (G < ngroups ? G : 0)];
-        return sr >= 0 ? -bv : 0.f;
+        return sr >= 0 ? bv : 0.f;
     }
 
     static __device__ void run(const GemmArgs &args)
@@ -1395,7 +1454,7 @@ struct Stream {
                 for (int t = 0; t < gspan; ++t)
                     sum += s_part[v][k * gspan + t];
                 const int G2 = (nb * BN + k * gspan * 16) / gs2;
-                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, sum);
+                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, -sum);
             }
         } else {
             if (g == 0) {

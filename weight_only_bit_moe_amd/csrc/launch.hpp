@@ -16,9 +16,9 @@ struct Workspace {
     int32_t *tile_expert;     // [max_tiles]
     int32_t *inv_perm;        // [P]
     uint16_t *x_perm;         // [T, H] bf16, fragment order per w13 group
-    float *x_bias;            // [T, H / g13]
+    float *x_bias;            // [T, H / g13] minus each group's bias term (chain start)
     uint16_t *act;            // [max_slots, I] bf16, fragment order per w2 group
-    float *act_bias;          // [max_slots, I / g2]
+    float *act_bias;          // [max_slots, I / g2] minus each group's bias term
     float *out_f32;           // [T, H]
     int32_t *chunk_counts;    // [align chunks][E + 1]: per-chunk expert counts, then invalid ids
 };
