@@ -40,6 +40,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
+
 constexpr int kMaxExperts = 1024;
 constexpr int kAlignThreads = 1024;
 
@@ -618,73 +619,76 @@ struct Tile {
     // Copies each wave issues per chunk: A pieces (16 slots shared by 8
     // waves; slots of inactive subtiles get harmless copies so every wave
     // issues the same number), its code pieces, its scales (one 2-byte copy
-    // per group) and, for waves below GPC, the bias terms of group `wave`.
+    // per group) and one bias copy.
     template <int MTA>
     static constexpr int a_copies() { return MTA <= 2 ? 1 : 2; }
     template <int MTA>
-    static constexpr int copies() { return a_copies<MTA>() + PIECES + GPC; }
+    static constexpr int copies() { return a_copies<MTA>() + PIECES + GPC + 1; }
 
+    // Copy item `idx` of chunk kc into `stage` (A pieces, then code pieces,
+    // then scales, then bias terms).  Callers pass a compile-time index
+    // (unrolled loops), so the branches fold away.
     template <int MTA>
-    static __device__ __forceinline__ void issue(int stage, const Ctx &cx, int kc)
+    static __device__ __forceinline__ void copy_item(int idx, int stage, const Ctx &cx, int kc)
     {
+        constexpr int NA = a_copies<MTA>();
         const uint32_t st = cx.ring + stage * STAGE;
-#pragma unroll
-        for (int k = 0; k < a_copies<MTA>(); ++k) {
-            const int slot = cx.wave + NW * k;   // [subtile][step]
-            copy_to_lds<16>(cx.a, cx.aoff[k] + (uint32_t)kc * (KC * 2),
+        if (idx < NA) {
+            const int slot = cx.wave + NW * idx;   // [subtile][step]
+            copy_to_lds<16>(cx.a, cx.aoff[idx] + (uint32_t)kc * (KC * 2),
                             st + A_OFF + slot * 64 * 16);
-        }
-        const uint32_t bw = st + B_OFF + cx.wave * B_WAVE;
-#pragma unroll
-        for (int k = 0; k < PIECES; ++k)
-            copy_to_lds<16>(cx.codes, cx.coff[k] + (uint32_t)kc * RB, bw + k * 64 * 16);
-#pragma unroll
-        for (int G = 0; G < GPC; ++G)
+        } else if (idx < NA + PIECES) {
+            const int k = idx - NA;
+            copy_to_lds<16>(cx.codes, cx.coff[k] + (uint32_t)kc * RB,
+                            st + B_OFF + cx.wave * B_WAVE + k * 64 * 16);
+        } else if (idx < NA + PIECES + GPC) {
+            const int G = idx - NA - PIECES;
             copy_to_lds<2>(cx.scales, cx.soff + (uint32_t)(kc * GPC + G) * 2u,
                            st + SC_OFF + (cx.wave * GPC + G) * 256);
-        if (cx.wave < GPC)
-            copy_to_lds<4>(cx.bias, cx.boff + (uint32_t)(kc * GPC + cx.wave) * 4u,
-                           st + BI_OFF + cx.wave * 256);
+        } else {
+            // every wave copies the bias terms of group wave % GPC (waves
+            // with the same group write identical values)
+            const int G = cx.wave % GPC;
+            copy_to_lds<4>(cx.bias, cx.boff + (uint32_t)(kc * GPC + G) * 4u,
+                           st + BI_OFF + G * 256);
+        }
     }
-
-    // Wait until this wave's copies of the chunk with `after` later chunks
-    // already issued have landed.
-    template <int L>
-    static __device__ __forceinline__ void wait_chunk_l(int after)
-    {
-        if (after >= 3)
-            wait_vm<3 * L>();
-        else if (after == 2)
-            wait_vm<2 * L>();
-        else if (after == 1)
-            wait_vm<L>();
-        else
-            wait_vm<0>();
-    }
+    // Copies of one chunk still to be issued: the chunk's stage and the
+    // chunk whose data goes there (past the last chunk, a repeat of the last
+    // chunk into a stage nobody reads any more, which keeps the number of
+    // copies per phase constant).
+    struct Pending {
+        int stage, kc;
+    };
     template <int MTA>
-    static __device__ __forceinline__ void wait_chunk(const Ctx &cx, int after)
+    static __device__ __forceinline__ void copy_items(int first, int last, const Ctx &cx,
+                                                      const Pending &pc)
     {
-        static_assert(3 * (copies<MTA>() + 1) < 64, "copies in flight exceed the wait counter");
-        if (cx.wave < GPC)
-            wait_chunk_l<copies<MTA>() + 1>(after);
-        else
-            wait_chunk_l<copies<MTA>()>(after);
+#pragma unroll
+        for (int t = first; t < last; ++t)
+            copy_item<MTA>(t, pc.stage, cx, pc.kc);
     }
 
     // VALU half: the chunk's codes of this wave's rows, unpacked into the
-    // B fragments of all KS steps.
+    // B fragments of all KS steps; copy items [C0, C1) of `pc` are spread
+    // over it.  Ends by reading the first row subtile's activation
+    // fragments and bias terms for the MFMA half.
+    template <int MTA, int C0, int C1>
     static __device__ __forceinline__ void unpack_chunk(const unsigned char *lds, int stage,
                                                         const Ctx &cx, bf16x8_t (&bf)[NT][KS],
-                                                        const UnpackConsts &magic)
+                                                        const UnpackConsts &magic,
+                                                        const Pending &pc, bf16x8_t (&af)[KS],
+                                                        f32x4_t (&nb)[GPC])
     {
         const int g = cx.g, c = cx.lane & 15;
-        const unsigned char *bw = lds + stage * STAGE + B_OFF + cx.wave * B_WAVE;
+        const unsigned char *st = lds + stage * STAGE;
+        const unsigned char *bw = st + B_OFF + cx.wave * B_WAVE;
 #pragma unroll
-        for (int G = 0; G < GPC; ++G) {
-            const int off = CodeTraits<BITS, GS>::dword_off(G, g) * 4;   // inside the row's chunk
+        for (int j = 0; j < NT; ++j) {
+            const int row = j * 16 + c;
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int row = j * 16 + c;
+            for (int G = 0; G < GPC; ++G) {
+                const int off = CodeTraits<BITS, GS>::dword_off(G, g) * 4;   // inside the row's chunk
                 const unsigned char *src =
                     bw + row * RB + (((off >> 4) ^ swz(row)) << 4) + (off & 15);
                 uint32_t q[NDW];
@@ -705,61 +709,61 @@ struct Tile {
                 for (int s = 0; s < S; ++s)
                     bf[j][G * S + s] = unpack<BITS, GS, NDW>(q, s, g, magic);
             }
+            copy_items<MTA>(C0 + j * (C1 - C0) / NT, C0 + (j + 1) * (C1 - C0) / NT, cx, pc);
+        }
+        load_subtile(st, cx, 0, af, nb);
+    }
+
+    // Activation fragments and (for groups of 64 or more) bias terms of row
+    // subtile i.
+    static constexpr bool PRE_BIAS = GPC <= 2;
+    static __device__ __forceinline__ void load_subtile(const unsigned char *st, const Ctx &cx,
+                                                        int i, bf16x8_t (&af)[KS],
+                                                        f32x4_t (&nb)[GPC])
+    {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            af[s] = *reinterpret_cast<const bf16x8_t *>(st + A_OFF +
+                                                       ((i * KS + s) * 64 + cx.lane) * 16);
+        if constexpr (PRE_BIAS) {
+#pragma unroll
+            for (int G = 0; G < GPC; ++G)
+                nb[G] = *reinterpret_cast<const f32x4_t *>(
+                    st + BI_OFF + (G * 64 + i * 16 + 4 * cx.g) * 4);
         }
     }
 
     // MFMA half: for each active row subtile and group, one chain per column
     // subtile starting from minus the bias term, folded into the
-    // accumulators with the group's scale.  The next subtile's activation
-    // fragments (and, for groups of 64 or more, bias terms) are read while
-    // the current one's MFMAs run, and the last fold of a subtile runs under
-    // the next subtile's MFMAs.
-    static constexpr bool PRE_BIAS = GPC <= 2;
-    template <int MTA>
+    // accumulators with the group's scale.  The next subtile's operands are
+    // read while the current one's MFMAs run, the last fold of a subtile runs
+    // under the next subtile's MFMAs, and copy items [C0, C1) of `pc` are
+    // spread over the subtiles.  af / nb hold subtile 0's operands on entry.
+    template <int MTA, int C0, int C1>
     static __device__ __forceinline__ void mfma_chunk(const unsigned char *lds, int stage,
                                                       const Ctx &cx, const bf16x8_t (&bf)[NT][KS],
-                                                      f32x4_t (&acc)[MTA][NT])
+                                                      f32x4_t (&acc)[MTA][NT], const Pending &pc,
+                                                      bf16x8_t (&af)[KS], f32x4_t (&nb)[GPC])
     {
-        const int lane = cx.lane, g = cx.g, c = lane & 15;
+        const int g = cx.g, c = cx.lane & 15;
         const unsigned char *st = lds + stage * STAGE;
         auto scales = [&](int G) {
             return *reinterpret_cast<const u32x4_t *>(
                 st + SC_OFF + ((cx.wave * GPC + G) * 64 + c * 4) * 4);
         };
-        auto bias = [&](int i, int G) {
-            return *reinterpret_cast<const f32x4_t *>(st + BI_OFF + (G * 64 + i * 16 + 4 * g) * 4);
-        };
-        bf16x8_t af[KS];
-        f32x4_t nb[GPC];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            af[s] = *reinterpret_cast<const bf16x8_t *>(st + A_OFF + (s * 64 + lane) * 16);
-        if constexpr (PRE_BIAS) {
-#pragma unroll
-            for (int G = 0; G < GPC; ++G)
-                nb[G] = bias(0, G);
-        }
         f32x4_t pend[NT];   // last chain of the previous subtile, not yet folded
 #pragma unroll
         for (int i = 0; i < MTA; ++i) {
             bf16x8_t an[KS];
             f32x4_t nbn[GPC];
-            if (i + 1 < MTA) {
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    an[s] = *reinterpret_cast<const bf16x8_t *>(
-                        st + A_OFF + (((i + 1) * KS + s) * 64 + lane) * 16);
-                if constexpr (PRE_BIAS) {
-#pragma unroll
-                    for (int G = 0; G < GPC; ++G)
-                        nbn[G] = bias(i + 1, G);
-                }
-            }
+            if (i + 1 < MTA)
+                load_subtile(st, cx, i + 1, an, nbn);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int G = 0; G < GPC; ++G) {
                 if constexpr (!PRE_BIAS)
-                    nb[G] = bias(i, G);
+                    nb[G] = *reinterpret_cast<const f32x4_t *>(
+                        st + BI_OFF + (G * 64 + i * 16 + 4 * g) * 4);
                 f32x4_t accg[NT];
 #pragma unroll
                 for (int s = 0; s < S; ++s)
@@ -777,6 +781,7 @@ struct Tile {
                         pend[j] = accg[j];
                 }
             }
+            copy_items<MTA>(C0 + i * (C1 - C0) / MTA, C0 + (i + 1) * (C1 - C0) / MTA, cx, pc);
             if (i + 1 < MTA) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
@@ -893,35 +898,12 @@ struct Tile {
 
     // The K loop and epilogue for a tile with MTA active 16-row subtiles.
     //
-    // Phases, separated by workgroup barriers (chunk k lives in stage
-    // k % STAGES):
-    //   phase -1:    waves 0-3 unpack chunk 0
-    //   phase 2k:    waves 0-3 run the MFMAs of chunk k, waves 4-7 unpack it
-    //   phase 2k+1:  waves 0-3 unpack chunk k+1, waves 4-7 run the MFMAs of k
-    // Every wave runs the same sequence (unpack 0, MFMAs 0, unpack 1, ...);
-    // waves 4-7 run it one phase later.  Chunk k is last read in phase
-    // 2k+1, so the copies of chunk k + STAGES go into its stage during phase
-    // 2k+2; chunk k+1 must have landed before the barrier that opens phase
-    // 2k+1.
-    template <int MTA>
-    static __device__ __forceinline__ void open_phase(const Ctx &cx, int p, int nchunks)
-    {
-        if (p & 1) {
-            const int j = (p - 1) >> 1;   // chunk j + 1 is read from this phase on
-            if (j + 1 < nchunks)
-                wait_chunk<MTA>(cx, min(STAGES - 2, nchunks - 2 - j));
-        }
-        workgroup_barrier();
-    }
-    // Copies issued during phase 2j (chunk j - 1 is no longer read): waves
-    // 4-7 issue them before their unpack, waves 0-3 after their MFMAs.
-    template <int MTA>
-    static __device__ __forceinline__ void issue_phase(const Ctx &cx, int j, int nchunks)
-    {
-        if (j >= 1 && j - 1 + STAGES < nchunks)
-            issue<MTA>((j - 1) % STAGES, cx, j - 1 + STAGES);
-    }
-
+    // Chunk k lives in stage k % STAGES.  One barrier per chunk: after the
+    // barrier that opens chunk k every wave is done with chunk k - 1, so the
+    // copies of chunk k - 1 + STAGES go into its stage while chunk k is
+    // unpacked and multiplied (spread over that work).  Before the next
+    // barrier each wave waits for its copies of chunk k + 1; the copies
+    // issued after those are always STAGES - 2 chunks' worth.
     template <int MTA>
     static __device__ void body(unsigned char *lds, const Rows &rows, const GemmArgs &args,
                                 const Ctx &cx)
@@ -935,35 +917,26 @@ struct Tile {
 
         const UnpackConsts magic = unpack_consts();
         const int nchunks = args.K / KC;
-        const int late = cx.wave >= 4 ? 1 : 0;   // waves 4-7 run one phase later
-        const bool on = cx.wave_on;
+        constexpr int L = copies<MTA>();
+        constexpr int V = L / 2;   // items issued during the unpack; the rest during the MFMAs
+        static_assert(STAGES * L < 64, "copies in flight exceed the wait counter");
+        auto last = [&](int c) { return c < nchunks ? c : nchunks - 1; };
 
 #pragma unroll
-        for (int p = 0; p < STAGES; ++p)
-            if (p < nchunks)
-                issue<MTA>(p, cx, p);
-        wait_chunk<MTA>(cx, min(STAGES - 1, nchunks - 1));
-        workgroup_barrier();   // opens phase -1
+        for (int p = 0; p < STAGES - 1; ++p)
+            copy_items<MTA>(0, L, cx, Pending{p, last(p)});
+        wait_vm<(STAGES - 2) * L>();   // chunk 0
 
         for (int k = 0; k < nchunks; ++k) {
-            bf16x8_t bf[NT][KS];
-            if (k > 0 || late)
-                open_phase<MTA>(cx, 2 * k - 1 + late, nchunks);
-            if (late)
-                issue_phase<MTA>(cx, k, nchunks);   // phase 2k: before the unpack
-            if (on)
-                unpack_chunk(lds, k % STAGES, cx, bf, magic);
-            open_phase<MTA>(cx, 2 * k + late, nchunks);
-            if (on) {
-                __builtin_amdgcn_s_setprio(1);
-                mfma_chunk<MTA>(lds, k % STAGES, cx, bf, acc);
-                __builtin_amdgcn_s_setprio(0);
-            }
-            if (!late)
-                issue_phase<MTA>(cx, k, nchunks);   // phase 2k: after the MFMAs
+            bf16x8_t bf[NT][KS], af[KS];
+            f32x4_t nb[GPC];
+            const Pending pc{(k + STAGES - 1) % STAGES, last(k + STAGES - 1)};
+            workgroup_barrier();
+            unpack_chunk<MTA, 0, V>(lds, k % STAGES, cx, bf, magic, pc, af, nb);
+            mfma_chunk<MTA, V, L>(lds, k % STAGES, cx, bf, acc, pc, af, nb);
+            wait_vm<(STAGES - 2) * L>();   // chunk k + 1
         }
-        if (!late)
-            open_phase<MTA>(cx, 2 * nchunks - 1, nchunks);   // waves 0-3 idle in the last phase
+        wait_vm<0>();   // repeats of the last chunk may still be in flight
         __syncthreads();   // every wave is done with the ring
 
         const int rows_real = rows.real;
