@@ -210,6 +210,20 @@ def test_token_without_valid_ids_gets_zero_output(dev, T, E):
     assert not G.to_f64(y)[1].any()
 
 
+@pytest.mark.parametrize("T,E", [(4, 8), (64, 4)])   # decode-shaped, prefill-shaped
+def test_all_ids_invalid_overwrites_output_with_zeros(dev, T, E):
+    """No tile at all: the output buffer (pre-filled with garbage) must still
+    be written, as the rounding of the zeroed sum."""
+    sp = spec(T=T, topk=2, E=E)
+    L = make_layer(sp, seed=79)
+    L.topk_ids[:, :] = -1
+    L.topk_ids[0, 1] = E
+    out = torch.full((sp.T, sp.H), 3.0, dtype=torch.bfloat16, device=dev)
+    y, got = G.run_layer(L, dev, out=out)
+    assert not G.to_f64(y).any()
+    G.assert_parity(got, O.forward_layer(L), "all ids invalid")
+
+
 def test_layer_empty_batch(dev):
     L = make_layer(spec(T=0), seed=1)
     y, _ = G.run_layer(L, dev)

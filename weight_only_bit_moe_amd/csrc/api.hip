@@ -47,7 +47,8 @@ int check_sizes(int T, int H, int I, int E, int topk)
 }
 
 struct Layout {
-    size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, ccounts, total;
+    size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, ccounts, done,
+        total;
 };
 
 Layout layout_of(int T, int H, int I, int E, int topk)
@@ -74,6 +75,7 @@ Layout layout_of(int T, int H, int I, int E, int topk)
     L.actbias = take(max_slots * (size_t)(I / kMinGroup) * sizeof(float));
     L.outf32 = take((size_t)T * H * sizeof(float));
     L.ccounts = take((size_t)wna16::align_chunks((long long)P) * (E + 1) * sizeof(int32_t));
+    L.done = take((size_t)H);   // one counter per 64 output columns, 64 bytes apart
     L.total = o;
     return L;
 }
@@ -254,6 +256,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.act_bias = reinterpret_cast<float *>(base + L.actbias);
     ws.out_f32 = reinterpret_cast<float *>(base + L.outf32);
     ws.chunk_counts = reinterpret_cast<int32_t *>(base + L.ccounts);
+    ws.done = reinterpret_cast<int32_t *>(base + L.done);
 
     wna16::KernelEvents ev[4];
     if (events)
@@ -266,11 +269,17 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
         MOE_WNA16_OK)
         return st;
-    if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream, ev[2]))) !=
-        MOE_WNA16_OK)
+    // Small outputs: the last w2 workgroup to finish rounds the sum to BF16
+    // itself, which saves the convert launch.  The profiled entry keeps the
+    // separate convert so that every step has its own events.
+    uint16_t *outb = static_cast<uint16_t *>(out);
+    const bool fuse = !events && d.variant2 == 2 && (size_t)T * H <= wna16::kFusedConvertMax;
+    if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream, ev[2],
+                                          fuse ? outb : nullptr))) != MOE_WNA16_OK)
         return st;
-    return hip_status(wna16::launch_convert(ws.out_f32, static_cast<uint16_t *>(out),
-                                            (size_t)T * H, stream, ev[3]));
+    if (fuse)
+        return MOE_WNA16_OK;
+    return hip_status(wna16::launch_convert(ws.out_f32, outb, (size_t)T * H, stream, ev[3]));
 }
 
 int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_w,

@@ -340,6 +340,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (size_t i = first; i < act_bias_n; i += nzero_threads)
         ws.act_bias[i] = 0.f;
+    for (size_t i = first; i < (size_t)H / 4; i += nzero_threads)
+        ws.done[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -363,6 +365,8 @@ struct GemmArgs {
     uint16_t *act_out;        // W13 epilogue
     float *act_bias_out;      // W13 epilogue
     float *out_f32;           // W2 epilogue
+    uint16_t *out_bf16;       // W2 decode epilogue: non-null -> the last workgroup converts
+    int32_t *done;            // W2 decode: finished workgroups per column block, 16 ints apart
     int K;                    // reduction length (H for w13, I for w2)
     int N;                    // output columns (I gate columns for w13, H for w2)
     int P, topk;
@@ -455,6 +459,15 @@ __device__ __forceinline__ bf16x8_t unpack(const uint32_t (&cw)[NDW], int s, int
         }
     }
     return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// FP32 -> BF16 (round to nearest even) of 4 consecutive values.
+__device__ __forceinline__ u32x2_t to_bf16x4(const f32x4_t v)
+{
+    u32x2_t o;
+    o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    return o;
 }
 
 __device__ __forceinline__ float swiglu(float g, float u, float alpha, float beta, float clamp)
@@ -1222,8 +1235,13 @@ struct Stream {
     {
         extern __shared__ __align__(16) unsigned char smem[];
         const int b = blockIdx.x;
-        if (b >= *args.num_tiles)
+        if (b >= *args.num_tiles) {
+            // no tile at all (every id invalid): the output is the zeroed sum
+            if constexpr (!W13)
+                if (args.out_bf16 && *args.num_tiles == 0 && b == 0)
+                    convert_block(args, blockIdx.y);
             return;
+        }
         const int K = args.K;
         const int ngroups = K / GS;
         const int lds_stride = K + 8;
@@ -1443,6 +1461,51 @@ struct Stream {
                         unsafeAtomicAdd(orow + nb * BN + wave * COLS + j * 16 + c, w * acc[j][v]);
                 }
             }
+            if (args.out_bf16)
+                arrive(args, *args.num_tiles, nb);
+        }
+    }
+
+    // Small outputs: every workgroup counts itself done in its column block
+    // once its atomics have been performed (each wave waits for them); the
+    // last one of the block rounds the block's columns of every token,
+    // reading them with device-coherent loads.  No cache flush is needed: the
+    // accumulator only ever changes through device-scope atomics.
+    static __device__ void arrive(const GemmArgs &args, int active, int nb)
+    {
+        __shared__ int last;
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's atomics are done
+        __syncthreads();
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(args.done + nb * 16, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == active - 1;
+        __syncthreads();
+        if (last)
+            convert_block(args, nb);
+    }
+    static __device__ void convert_block(const GemmArgs &args, int nb)
+    {
+        constexpr int Q = BN / 4;   // float4 per token row in the block
+        const int n4 = (args.P / args.topk) * Q;
+        for (int i0 = threadIdx.x; i0 < n4; i0 += 4 * NTHREADS) {
+            f32x4_t v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * NTHREADS;
+                const size_t e = (size_t)(i / Q) * args.N + nb * BN + (i % Q) * 4;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    v[k][t] = i < n4 ? __hip_atomic_load(args.out_f32 + e + t, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + k * NTHREADS;
+                const size_t e = (size_t)(i / Q) * args.N + nb * BN + (i % Q) * 4;
+                if (i < n4)
+                    *reinterpret_cast<u32x2_t *>(args.out_bf16 + e) = to_bf16x4(v[k]);
+            }
         }
     }
 };
@@ -1460,11 +1523,7 @@ __global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restri
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4)
         return;
-    const f32x4_t v = reinterpret_cast<const f32x4_t *>(src)[i];
-    u32x2_t o;
-    o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    reinterpret_cast<u32x2_t *>(dst)[i] = o;
+    reinterpret_cast<u32x2_t *>(dst)[i] = to_bf16x4(reinterpret_cast<const f32x4_t *>(src)[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1540,6 +1599,7 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
         // load units in flight per wave: as many as fit without spilling
         constexpr int D = Stream<BITS, GS, NB, 1, W13>::SPLIT      ? 1
                           : Stream<BITS, GS, NB, 1, W13>::GPU == 4 ? 2
+                          : BITS == 4 && GS == 128                 ? 8
                                                                    : 4;
         using K_ = Stream<BITS, GS, NB, D, W13>;
         using K1 = Stream<BITS, GS, NB, 1, W13>;
@@ -1604,7 +1664,7 @@ hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &
 
 hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
                      const LayerDims &d, const Workspace &ws, hipStream_t stream,
-                     const KernelEvents &ev)
+                     const KernelEvents &ev, uint16_t *out_bf16)
 {
     GemmArgs a{};
     a.a = ws.act;
@@ -1616,6 +1676,8 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
     a.num_tiles = ws.meta;
     a.topk_w = topk_w;
     a.out_f32 = ws.out_f32;
+    a.out_bf16 = out_bf16;
+    a.done = ws.done;
     a.K = d.I;
     a.N = d.H;
     a.P = d.T * d.topk;

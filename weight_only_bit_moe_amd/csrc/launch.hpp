@@ -21,6 +21,7 @@ struct Workspace {
     float *act_bias;          // [max_slots, I / g2] minus each group's bias term
     float *out_f32;           // [T, H]
     int32_t *chunk_counts;    // [align chunks][E + 1]: per-chunk expert counts, then invalid ids
+    int32_t *done;            // [H / 64][16]: decode w2 workgroups finished per column block
 };
 
 // Pairs per workgroup of the expert sort.
@@ -47,10 +48,15 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
 // Fused gate/up WNA16 GEMM with the SwiGLU epilogue.
 hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
                       const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
-// Down WNA16 GEMM with the routing-weighted FP32 scatter-add epilogue.
+// Down WNA16 GEMM with the routing-weighted FP32 scatter-add epilogue.  With
+// a non-null out_bf16 (decode-shaped w2 and T*H <= kFusedConvertMax only) the
+// last workgroup to finish also writes the BF16 output.
 hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
                      const LayerDims &d, const Workspace &ws, hipStream_t stream,
-                     const KernelEvents &ev);
+                     const KernelEvents &ev, uint16_t *out_bf16 = nullptr);
+// Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
+// workgroup of each column block rounds that block).
+constexpr size_t kFusedConvertMax = 1 << 18;
 // FP32 accumulator -> BF16 output (round to nearest even).
 hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,
                           const KernelEvents &ev);
