@@ -48,7 +48,7 @@ int check_sizes(int T, int H, int I, int E, int topk)
 
 struct Layout {
     size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, ccounts, done,
-        total;
+        tdone, total;
 };
 
 Layout layout_of(int T, int H, int I, int E, int topk)
@@ -76,6 +76,7 @@ Layout layout_of(int T, int H, int I, int E, int topk)
     L.outf32 = take((size_t)T * H * sizeof(float));
     L.ccounts = take((size_t)wna16::align_chunks((long long)P) * (E + 1) * sizeof(int32_t));
     L.done = take((size_t)H);   // one counter per 64 output columns, 64 bytes apart
+    L.tdone = take(max_tiles * 64);   // one counter per tile, 64 bytes apart
     L.total = o;
     return L;
 }
@@ -257,6 +258,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.out_f32 = reinterpret_cast<float *>(base + L.outf32);
     ws.chunk_counts = reinterpret_cast<int32_t *>(base + L.ccounts);
     ws.done = reinterpret_cast<int32_t *>(base + L.done);
+    ws.tile_done = reinterpret_cast<int32_t *>(base + L.tdone);
 
     wna16::KernelEvents ev[4];
     if (events)
@@ -266,14 +268,28 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, ev[0]))) !=
         MOE_WNA16_OK)
         return st;
-    if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
-        MOE_WNA16_OK)
-        return st;
     // Small outputs: the last w2 workgroup to finish rounds the sum to BF16
     // itself, which saves the convert launch.  The profiled entry keeps the
     // separate convert so that every step has its own events.
     uint16_t *outb = static_cast<uint16_t *>(out);
     const bool fuse = !events && d.variant2 == 2 && (size_t)T * H <= wna16::kFusedConvertMax;
+    // Decode shapes on the plain entry point: both GEMMs in one launch when
+    // the two projections share a format (the profiled entry keeps one
+    // launch per step).
+    hipError_t he = hipErrorNotSupported;
+    if (!events)
+        he = wna16::launch_decode(w13_packed, w13_scales, w2_packed, w2_scales, topk_w, d, ws,
+                                  stream, fuse ? outb : nullptr);
+    if (he != hipErrorNotSupported) {
+        if ((st = hip_status(he)) != MOE_WNA16_OK)
+            return st;
+        if (fuse)
+            return MOE_WNA16_OK;
+        return hip_status(wna16::launch_convert(ws.out_f32, outb, (size_t)T * H, stream, ev[3]));
+    }
+    if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
+        MOE_WNA16_OK)
+        return st;
     if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream, ev[2],
                                           fuse ? outb : nullptr))) != MOE_WNA16_OK)
         return st;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
 template <int BITS, int GS>
 __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int T, int H, int topk,
-    int E, int bm, int nalign, int nprep, size_t act_bias_n, Workspace ws)
+    int E, int bm, int nalign, int nprep, size_t act_bias_n, int tdone_n, Workspace ws)
 {
     __shared__ AlignShared sh;
     const int blk = blockIdx.x;
@@ -342,6 +342,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         ws.act_bias[i] = 0.f;
     for (size_t i = first; i < (size_t)H / 4; i += nzero_threads)
         ws.done[i] = 0;
+    for (size_t i = first; i < (size_t)tdone_n; i += nzero_threads)
+        ws.tile_done[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -367,6 +369,8 @@ struct GemmArgs {
     float *out_f32;           // W2 epilogue
     uint16_t *out_bf16;       // W2 decode epilogue: non-null -> the last workgroup converts
     int32_t *done;            // W2 decode: finished workgroups per column block, 16 ints apart
+    int32_t *tile_done;       // fused decode: w13 workgroups finished per tile, 16 ints apart
+    int tile_target;          // fused decode w2: w13 workgroups per tile
     int K;                    // reduction length (H for w13, I for w2)
     int N;                    // output columns (I gate columns for w13, H for w2)
     int P, topk;
@@ -1077,7 +1081,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // holds, for each group of the unit, the dwords its MFMA fragments need
 // (dwords [g*n, g*n + n) of the group with n = gs*bits/128).
 // ---------------------------------------------------------------------------
-template <int BITS, int GS, int NB, int D, bool W13>
+template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false>
 struct Stream {
     static constexpr int R = 4;                      // rows per tile
     static constexpr int NW = 4;                     // waves per workgroup
@@ -1227,19 +1231,37 @@ struct Stream {
         const int G = i / R, r = i % R;
         int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
         sr = i < R * ngroups ? sr : -1;
-        const float bv = args.a_bias[(size_t)(sr >= 0 ? sr : 0) * ngroups + (G < ngroups ? G : 0)];
+        const float *bp = args.a_bias + (size_t)(sr >= 0 ? sr : 0) * ngroups + (G < ngroups ? G : 0);
+        float bv;
+        if constexpr (FUSED && !W13)   // written by this launch's w13 items
+            bv = __hip_atomic_load(bp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            bv = *bp;
         return sr >= 0 ? bv : 0.f;
     }
 
-    static __device__ void run(const GemmArgs &args)
+    // 16 bytes of an activation row; device-coherent loads in the fused w2,
+    // whose act rows were written by other workgroups of the same launch
+    static __device__ __forceinline__ u32x4_t load_a(const uint16_t *p)
+    {
+        if constexpr (FUSED && !W13) {
+            const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+            const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+        } else {
+            return *reinterpret_cast<const u32x4_t *>(p);
+        }
+    }
+
+    static __device__ void run(const GemmArgs &args, int b, int nb)
     {
         extern __shared__ __align__(16) unsigned char smem[];
-        const int b = blockIdx.x;
         if (b >= *args.num_tiles) {
             // no tile at all (every id invalid): the output is the zeroed sum
             if constexpr (!W13)
                 if (args.out_bf16 && *args.num_tiles == 0 && b == 0)
-                    convert_block(args, blockIdx.y);
+                    convert_block(args, nb);
             return;
         }
         const int K = args.K;
@@ -1256,7 +1278,6 @@ struct Stream {
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int c = lane & 15, g = lane >> 4;
         const int e = args.tile_expert[b];
-        const int nb = blockIdx.y;
         // rows of the tile (uniform loads; padding rows have pair index P)
         int src[R], pair[R];
         int rows_real = 0;
@@ -1289,6 +1310,21 @@ struct Stream {
         for (int d = 0; d < D; ++d)
             load_unit(q[d], brow, d, g);
 
+        if constexpr (FUSED && !W13) {
+            // the tile's act rows and bias terms come from this launch's w13
+            // items: wait (bounded) until all of them are done
+            if (tid == 0) {
+                const int32_t *cnt = args.tile_done + b * 16;
+                for (int it = 0; it < (1 << 22); ++it) {
+                    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                        args.tile_target)
+                        break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+        }
+
         // Activation rows (zero for padding rows), their bias terms and this
         // workgroup's scales go to LDS.  Each pass issues all of its loads
         // before its first LDS store, so the latencies overlap; the first bias
@@ -1315,8 +1351,7 @@ struct Stream {
                     for (int r = 0; r < R; ++r) {
                         v[t][r] = u32x4_t{0u, 0u, 0u, 0u};
                         if (src[r] >= 0 && k8 < k8n)
-                            v[t][r] = reinterpret_cast<const u32x4_t *>(args.a +
-                                                                        (size_t)src[r] * K)[k8];
+                            v[t][r] = load_a(args.a + (size_t)src[r] * K + (size_t)k8 * 8);
                     }
                     vs[t] = u32x4_t{0u, 0u, 0u, 0u};
                     if (k8 < spieces) {
@@ -1422,7 +1457,12 @@ struct Stream {
                     if (g == 0 && v < rows_real) {
                         a = swiglu(acc[j][v], acc[NG + j][v], args.alpha, args.beta, args.clamp);
                         const uint32_t st = bf16_scaled(f32_to_bf16(a), esh);
-                        args.act_out[(size_t)(b * R + v) * args.N + pos] = (uint16_t)st;
+                        uint16_t *dst = args.act_out + (size_t)(b * R + v) * args.N + pos;
+                        if constexpr (FUSED)   // read by w2 workgroups of this launch
+                            __hip_atomic_store(dst, (uint16_t)st, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *dst = (uint16_t)st;
                         a = bf16_to_f32(st) * wgt;
                     }
                     // sum of the 16 columns of this subtile (lanes 0..15)
@@ -1446,6 +1486,15 @@ struct Stream {
                     sum += s_part[v][k * gspan + t];
                 const int G2 = (nb * BN + k * gspan * 16) / gs2;
                 unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, -sum);
+            }
+            if constexpr (FUSED) {
+                // act and its bias terms are performed (device scope): count
+                // this workgroup done for its tile
+                __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_fetch_add(args.tile_done + b * 16, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
         } else {
             if (g == 0) {
@@ -1514,7 +1563,23 @@ template <int BITS, int GS, int NB, int D, bool W13>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void stream_kernel(
     const GemmArgs args)
 {
-    Stream<BITS, GS, NB, D, W13>::run(args);
+    Stream<BITS, GS, NB, D, W13>::run(args, blockIdx.x, blockIdx.y);
+}
+
+// Both decode-shaped GEMMs in one launch: workgroups [0, n13) are the w13
+// (tile, column block) items, tile-major, the rest the w2 items.  Workgroups
+// are dispatched in id order, so every w13 item has been dispatched before
+// any w2 item waits for its tile's w13 items; a w2 item streams its first
+// weights while it waits.
+template <int B13, int G13, int D13, int B2, int G2, int D2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_kernel(
+    const GemmArgs a13, const GemmArgs a2, int max_tiles, int nblk13, int nblk2)
+{
+    const int id = blockIdx.x, n13 = max_tiles * nblk13;
+    if (id < n13)
+        Stream<B13, G13, 2, D13, true, true>::run(a13, id / nblk13, id % nblk13);
+    else
+        Stream<B2, G2, 2, D2, false, true>::run(a2, (id - n13) / nblk2, (id - n13) % nblk2);
 }
 
 __global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restrict__ dst,
@@ -1568,7 +1633,7 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
                           d.topk, d.E, d.block_m, nalign, nprep,
                           // only the decode-shaped w13 adds into act_bias
                           d.variant13 == 2 ? (size_t)d.max_tiles * d.block_m * (d.I / d.g2) : 0,
-                          ws);
+                          d.max_tiles * 16, ws);
     return hipGetLastError();
 }
 
@@ -1587,6 +1652,15 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
     }
 }
 
+// Load units in flight per wave of the decode-shaped kernel: as many as fit
+// without spilling.
+template <int BITS, int GS, bool W13>
+static constexpr int stream_depth()
+{
+    using S1 = Stream<BITS, GS, 2, 1, W13>;
+    return S1::SPLIT ? 1 : S1::GPU == 4 ? 2 : (BITS == 4 && GS == 128) ? 8 : 4;
+}
+
 // Tile shapes.  Variant 2 (few rows per expert, HBM-bound): the stream kernel
 // on 4-row tiles.  Variant 1 (many rows per expert, MFMA-bound): the tile
 // kernel on 64-row tiles.
@@ -1596,11 +1670,7 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
 {
     if (variant == 2) {
         constexpr int NB = 2;
-        // load units in flight per wave: as many as fit without spilling
-        constexpr int D = Stream<BITS, GS, NB, 1, W13>::SPLIT      ? 1
-                          : Stream<BITS, GS, NB, 1, W13>::GPU == 4 ? 2
-                          : BITS == 4 && GS == 128                 ? 8
-                                                                   : 4;
+        constexpr int D = stream_depth<BITS, GS, W13>();
         using K_ = Stream<BITS, GS, NB, D, W13>;
         using K1 = Stream<BITS, GS, NB, 1, W13>;
         const dim3 grid(max_tiles, a.N / K_::BN);
@@ -1637,8 +1707,8 @@ static hipError_t gemm_select(const GemmArgs &a, int bits, int gs, int variant, 
     }
 }
 
-hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
-                      const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
+static GemmArgs w13_args(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
+                         const Workspace &ws)
 {
     GemmArgs a{};
     a.a = ws.x_perm;
@@ -1659,12 +1729,19 @@ hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &
     a.alpha = d.alpha;
     a.beta = d.beta;
     a.clamp = d.clamp;
-    return gemm_select<true>(a, d.bits13, d.g13, d.variant13, d.max_tiles, stream, ev);
+    a.tile_done = ws.tile_done;
+    return a;
 }
 
-hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
-                     const LayerDims &d, const Workspace &ws, hipStream_t stream,
-                     const KernelEvents &ev, uint16_t *out_bf16)
+hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
+                      const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
+{
+    return gemm_select<true>(w13_args(w13, s13, d, ws), d.bits13, d.g13, d.variant13,
+                             d.max_tiles, stream, ev);
+}
+
+static GemmArgs w2_args(const int32_t *w2, const uint16_t *s2, const float *topk_w,
+                        const LayerDims &d, const Workspace &ws, uint16_t *out_bf16)
 {
     GemmArgs a{};
     a.a = ws.act;
@@ -1682,7 +1759,53 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
     a.N = d.H;
     a.P = d.T * d.topk;
     a.topk = d.topk;
-    return gemm_select<false>(a, d.bits2, d.g2, d.variant2, d.max_tiles, stream, ev);
+    a.tile_done = ws.tile_done;
+    return a;
+}
+
+hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
+                     const LayerDims &d, const Workspace &ws, hipStream_t stream,
+                     const KernelEvents &ev, uint16_t *out_bf16)
+{
+    return gemm_select<false>(w2_args(w2, s2, topk_w, d, ws, out_bf16), d.bits2, d.g2,
+                              d.variant2, d.max_tiles, stream, ev);
+}
+
+template <int BITS, int GS>
+static hipError_t decode_dispatch(const GemmArgs &a13, GemmArgs a2, int max_tiles,
+                                  hipStream_t stream)
+{
+    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
+    using S13 = Stream<BITS, GS, 2, D13, true, true>;
+    using S2 = Stream<BITS, GS, 2, D2, false, true>;
+    if ((a13.K / S13::UK) % D13 != 0 || (a2.K / S2::UK) % D2 != 0)
+        return hipErrorNotSupported;
+    const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
+    a2.tile_target = nblk13;
+    const size_t l13 = S13::lds_bytes(a13.K), l2 = S2::lds_bytes(a2.K);
+    hipExtLaunchKernelGGL((decode_kernel<BITS, GS, D13, BITS, GS, D2>),
+                          dim3((unsigned)(max_tiles * (nblk13 + nblk2))), dim3(S13::NTHREADS),
+                          (uint32_t)(l13 > l2 ? l13 : l2), stream, nullptr, nullptr, 0, a13, a2,
+                          max_tiles, nblk13, nblk2);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t *w2,
+                         const uint16_t *s2, const float *topk_w, const LayerDims &d,
+                         const Workspace &ws, hipStream_t stream, uint16_t *out_bf16)
+{
+    if (d.variant13 != 2 || d.variant2 != 2 || d.bits13 != d.bits2 || d.g13 != d.g2)
+        return hipErrorNotSupported;
+    const GemmArgs a13 = w13_args(w13, s13, d, ws);
+    const GemmArgs a2 = w2_args(w2, s2, topk_w, d, ws, out_bf16);
+    switch (d.bits13 * 1000 + d.g13) {   // 2-bit g32: both bodies do not fit one kernel's registers
+    case 2064: return decode_dispatch<2, 64>(a13, a2, d.max_tiles, stream);
+    case 2128: return decode_dispatch<2, 128>(a13, a2, d.max_tiles, stream);
+    case 4032: return decode_dispatch<4, 32>(a13, a2, d.max_tiles, stream);
+    case 4064: return decode_dispatch<4, 64>(a13, a2, d.max_tiles, stream);
+    case 4128: return decode_dispatch<4, 128>(a13, a2, d.max_tiles, stream);
+    default: return hipErrorNotSupported;
+    }
 }
 
 size_t decode_lds_bytes(int K, int gs)

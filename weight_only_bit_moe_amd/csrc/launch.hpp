@@ -22,6 +22,7 @@ struct Workspace {
     float *out_f32;           // [T, H]
     int32_t *chunk_counts;    // [align chunks][E + 1]: per-chunk expert counts, then invalid ids
     int32_t *done;            // [H / 64][16]: decode w2 workgroups finished per column block
+    int32_t *tile_done;       // [max_tiles][16]: fused decode, w13 workgroups finished per tile
 };
 
 // Pairs per workgroup of the expert sort.
@@ -54,6 +55,12 @@ hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &
 hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
                      const LayerDims &d, const Workspace &ws, hipStream_t stream,
                      const KernelEvents &ev, uint16_t *out_bf16 = nullptr);
+// Both decode-shaped GEMMs in one launch (same bits and group on both
+// projections); hipErrorNotSupported, before any launch, when the shapes do
+// not allow it.  out_bf16 as for launch_w2.
+hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t *w2,
+                         const uint16_t *s2, const float *topk_w, const LayerDims &d,
+                         const Workspace &ws, hipStream_t stream, uint16_t *out_bf16);
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
