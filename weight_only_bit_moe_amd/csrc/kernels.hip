@@ -1257,10 +1257,19 @@ struct Stream {
     static __device__ void run(const GemmArgs &args, int b, int nb)
     {
         extern __shared__ __align__(16) unsigned char smem[];
-        if (b >= *args.num_tiles) {
+        // the tile count, the tile's expert and its rows load together (one
+        // round trip; b < max_tiles keeps the last two in bounds, their
+        // values are unused past the last tile)
+        const int ntiles = *args.num_tiles;
+        const int e = args.tile_expert[b];
+        int pair[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            pair[r] = args.sorted_ids[b * R + r];
+        if (b >= ntiles) {
             // no tile at all (every id invalid): the output is the zeroed sum
             if constexpr (!W13)
-                if (args.out_bf16 && *args.num_tiles == 0 && b == 0)
+                if (args.out_bf16 && ntiles == 0 && b == 0)
                     convert_block(args, nb);
             return;
         }
@@ -1277,13 +1286,11 @@ struct Stream {
 
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int c = lane & 15, g = lane >> 4;
-        const int e = args.tile_expert[b];
-        // rows of the tile (uniform loads; padding rows have pair index P)
-        int src[R], pair[R];
+        // rows of the tile (padding rows have pair index P)
+        int src[R];
         int rows_real = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            pair[r] = args.sorted_ids[b * R + r];
             const bool real = pair[r] < args.P;
             src[r] = real ? (W13 ? pair[r] / args.topk : b * R + r) : -1;
             rows_real += real ? 1 : 0;
@@ -1511,7 +1518,7 @@ struct Stream {
                 }
             }
             if (args.out_bf16)
-                arrive(args, *args.num_tiles, nb);
+                arrive(args, ntiles, nb);
         }
     }
 
