@@ -36,7 +36,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
-KERNELS = ("route", "w13", "w2", "convert")
 KERNEL_SOURCE = os.path.join(ROOT, "weight_only_bit_moe_amd", "csrc", "kernels.hip")
 
 
@@ -110,7 +109,7 @@ def kernel_traffic(path, kernel):
     text = open(path).read()
     want = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(rf"traffic_bytes_per_launch\[{kernel}\]:\s*([0-9.eE+]+)", text)
+    m_b = re.search(rf"traffic_bytes_per_launch\[{re.escape(kernel)}\]:\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b or m_sha.group(1) != want:
         return None
     return float(m_b.group(1))
@@ -208,13 +207,21 @@ def main():
     t3 = time.perf_counter()
     ms_events = (t3 - t2) * 1e3 / steps
 
-    kern_ms = {name: [] for name in KERNELS}
+    # one entry per launch: steps that share a launch (plan: gemms_one_launch,
+    # convert_in_w2) are timed as that launch
+    one = bool(plan["gemms_one_launch"])
+    launches = [("route", 0, 1)]
+    launches += [("w13+w2", 2, 5)] if one else [("w13", 2, 3), ("w2", 4, 5)]
+    if not plan["convert_in_w2"]:
+        launches.append(("convert", 6, 7))
+    kern_ms = {name: [] for name, _, _ in launches}
     step_gpu_ms = []
+    last_stop = launches[-1][2]
     for i in range(steps):
         ev = events[i]
-        for j, name in enumerate(KERNELS):
-            kern_ms[name].append(hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]))
-        step_gpu_ms.append(hip.elapsed_ms(ev[0], ev[7]))
+        for name, a0, a1 in launches:
+            kern_ms[name].append(hip.elapsed_ms(ev[a0], ev[a1]))
+        step_gpu_ms.append(hip.elapsed_ms(ev[0], ev[last_stop]))
     avg = {n: float(np.mean(v)) for n, v in kern_ms.items()}
 
     # algorithmic work of each step (bookkeeping from the routing ids)
@@ -230,10 +237,12 @@ def main():
         "w2": mean_touched * b2 + P * I * 2 + T * H * 4,
     }
     alg_flops = {"w13": 2.0 * P * 2 * I * H, "w2": 2.0 * P * H * I}
+    alg_bytes["w13+w2"] = alg_bytes["w13"] + alg_bytes["w2"]
+    alg_flops["w13+w2"] = alg_flops["w13"] + alg_flops["w2"]
     layer_bytes = mean_touched * (b13 + b2) + T * H * 2 * 2
     layer_flops = alg_flops["w13"] + alg_flops["w2"]
 
-    dom = max(("w13", "w2"), key=lambda n: avg[n])
+    dom = max((n for n in avg if n.startswith("w")), key=lambda n: avg[n])
     if decode:
         achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -247,7 +256,7 @@ def main():
     roof["algorithmic_bytes" if decode else "algorithmic_flops"] = (
         alg_bytes[dom] if decode else alg_flops[dom])
     traffic_file = args.traffic_file or os.path.join(
-        ROOT, "profiles", f"{dom}_{sp.name}_counters.md")
+        ROOT, "profiles", f"counters_{sp.name}.md")
     roof["traffic"] = kernel_traffic(traffic_file, dom)
 
     value = T / (ms_per_step * 1e-3)
@@ -270,8 +279,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "kernel_ms": avg,
-        "kernel_timing": "HIP events in each kernel's dispatch packet, second pass of the "
-                         "same K steps on the same stream",
+        "kernel_timing": "HIP events in each launch's dispatch packet, second pass of the "
+                         "same K steps (same kernels) on the same stream",
         "ms_per_step_with_events": ms_events,
         "gpu_ms_per_step_events": float(np.mean(step_gpu_ms)),
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -76,6 +76,10 @@ typedef struct {
     int32_t w13_variant;    /* 2: decode-shaped (4-row tiles, weight streaming),    */
                             /* 1: prefill-shaped (64-row MFMA tiles)                */
     int32_t w2_variant;     /* same encoding for the down projection               */
+    int32_t gemms_one_launch; /* 1: both decode-shaped GEMMs run in one launch      */
+                              /*    (same bits and group on both projections)      */
+    int32_t convert_in_w2;  /* 1: the BF16 rounding runs inside the decode w2       */
+                            /*    launch (decode shapes with T*H <= 2^18)          */
 } moe_wna16_plan_t;
 
 /*
@@ -121,12 +125,19 @@ int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
- * moe_wna16_forward with per-kernel timing.  `events` is a HOST array of 8
- * caller-created hipEvent_t; the four kernels of the layer (in order: routing
- * and activation reorder, w13 + SwiGLU, w2 + scatter-add, BF16 convert) record
- * events[2i] when kernel i starts and events[2i+1] when it ends, from the
- * dispatch packets themselves (no extra packets on the stream).  Same checks
- * and status codes as moe_wna16_forward, plus EINVAL for a NULL `events`.
+ * moe_wna16_forward with per-step timing; it launches the same kernels as
+ * moe_wna16_forward.  `events` is a HOST array of 8 caller-created
+ * hipEvent_t; for the four steps of the layer (in order: routing and
+ * activation reorder, w13 + SwiGLU, w2 + scatter-add, BF16 rounding) step i
+ * records events[2i] when its launch starts and events[2i+1] when it ends,
+ * from the dispatch packets themselves (no extra packets on the stream).
+ * Steps that share a launch (see moe_wna16_plan_t: gemms_one_launch,
+ * convert_in_w2): the launch records the first step's start event and the
+ * last step's stop event, and the events in between are not recorded; so
+ * with gemms_one_launch, events[2] and events[5] bracket the one w13 + w2
+ * launch, and with convert_in_w2, events[6] and events[7] stay unrecorded
+ * (the rounding is inside the w2 launch).  Same checks and status codes as
+ * moe_wna16_forward, plus EINVAL for a NULL `events`.
  */
 int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const float *topk_w,
                                const int32_t *w13_packed, const uint16_t *w13_scales,

@@ -63,6 +63,21 @@ def test_plan_picks_tiles_from_rows_per_expert(lib):
     assert big["w13_variant"] == 1
 
 
+def test_plan_reports_shared_launches(lib):
+    dec = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (2, 128), (2, 128))
+    assert dec["gemms_one_launch"] == 1 and dec["convert_in_w2"] == 1
+    bdec = M.moe_wna16_plan(64, 4096, 2048, 256, 6, (4, 128), (4, 128))
+    assert bdec["gemms_one_launch"] == 1 and bdec["convert_in_w2"] == 1   # 64*4096 <= 2^18
+    big_t = M.moe_wna16_plan(128, 4096, 2048, 256, 6, (4, 128), (4, 128))
+    assert big_t["w13_variant"] == 2 and big_t["convert_in_w2"] == 0
+    mixed = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (4, 128), (2, 128))
+    assert mixed["w13_variant"] == 2 and mixed["gemms_one_launch"] == 0
+    g32 = M.moe_wna16_plan(4, 1024, 512, 256, 6, (2, 32), (2, 32))
+    assert g32["w13_variant"] == 2 and g32["gemms_one_launch"] == 0
+    pre = M.moe_wna16_plan(2048, 4096, 2048, 256, 6, (2, 128), (2, 128))
+    assert pre["gemms_one_launch"] == 0 and pre["convert_in_w2"] == 0
+
+
 NAN, INF = float("nan"), math.inf
 GOOD = dict(T=4, H=256, I=128, E=8, topk=2, q13=(4, 128), q2=(4, 128), alpha=1.0, beta=0.0,
             clamp=INF)

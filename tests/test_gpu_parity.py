@@ -185,8 +185,9 @@ def test_layer_matches_oracle(dev, name):
     G.assert_parity(got, ref, name)
 
 
-def test_layer_empty_experts_invalid_and_duplicate_ids(dev):
-    sp = spec(T=10, topk=3, E=8)
+@pytest.mark.parametrize("HI", [256, 1024])   # decode GEMMs in separate / shared launches
+def test_layer_empty_experts_invalid_and_duplicate_ids(dev, HI):
+    sp = spec(T=10, H=HI, I=HI, topk=3, E=8)
     L = make_layer(sp, seed=77)
     ids = L.topk_ids.copy()
     ids[0, 1] = -1
@@ -210,11 +211,12 @@ def test_token_without_valid_ids_gets_zero_output(dev, T, E):
     assert not G.to_f64(y)[1].any()
 
 
-@pytest.mark.parametrize("T,E", [(4, 8), (64, 4)])   # decode-shaped, prefill-shaped
-def test_all_ids_invalid_overwrites_output_with_zeros(dev, T, E):
+@pytest.mark.parametrize("T,E,HI", [(4, 8, 256), (4, 8, 1024), (64, 4, 256)])
+def test_all_ids_invalid_overwrites_output_with_zeros(dev, T, E, HI):
     """No tile at all: the output buffer (pre-filled with garbage) must still
-    be written, as the rounding of the zeroed sum."""
-    sp = spec(T=T, topk=2, E=E)
+    be written, as the rounding of the zeroed sum (decode shapes with separate
+    and with shared GEMM launches, and prefill shapes)."""
+    sp = spec(T=T, H=HI, I=HI, topk=2, E=E)
     L = make_layer(sp, seed=79)
     L.topk_ids[:, :] = -1
     L.topk_ids[0, 1] = E
@@ -222,6 +224,49 @@ def test_all_ids_invalid_overwrites_output_with_zeros(dev, T, E):
     y, got = G.run_layer(L, dev, out=out)
     assert not G.to_f64(y).any()
     G.assert_parity(got, O.forward_layer(L), "all ids invalid")
+
+
+@pytest.mark.parametrize("T,E,HI,q", [(4, 8, 1024, (2, 128)), (4, 8, 1024, (4, 64)),
+                                      (4, 8, 256, (4, 128)), (64, 4, 256, (4, 128))])
+def test_profiled_entry_matches_plain_and_records_events(dev, T, E, HI, q):
+    """The profiled entry launches the same kernels: same parity, and every
+    event pair brackets a non-negative interval, launches in stream order."""
+    import ctypes
+
+    from bench import Hip
+
+    sp = spec(T=T, H=HI, I=HI, topk=2, E=E, bits13=q[0], group13=q[1], bits2=q[0], group2=q[1])
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, q, q)
+    assert plan["gemms_one_launch"] == (1 if HI == 1024 else 0)
+    L = make_layer(sp, seed=80)
+    d = G.to_device(L, dev)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    out = torch.empty((sp.T, sp.H), dtype=torch.bfloat16, device=dev)
+    hip = Hip()
+    ev = (ctypes.c_void_p * 8)(*[hip.event() for _ in range(8)])
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    clamp = None if math.isinf(sp.clamp) else sp.clamp
+    st = M.moe_wna16_forward_profiled(
+        d["x"].data_ptr(), d["topk_ids"].data_ptr(), d["topk_w"].data_ptr(), d["w13"].data_ptr(),
+        d["s13"].data_ptr(), d["w2"].data_ptr(), d["s2"].data_ptr(), sp.T, sp.H, sp.I, sp.E,
+        sp.topk, (sp.bits13, sp.group13), (sp.bits2, sp.group2), sp.alpha, sp.beta, sp.clamp,
+        out.data_ptr(), ws.data_ptr(), ws.numel(), stream, ev)
+    assert st == 0
+    torch.cuda.synchronize(dev)
+    f32 = M.workspace_f32_sum(ws, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
+    bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits, G.f32_to_bf16_bits(f32))
+    G.assert_parity(f32.astype(np.float64), O.forward_layer(L), "profiled entry")
+    # launches in stream order: (start, stop) event indices of each launch
+    launches = [(0, 1)] + ([(2, 5)] if plan["gemms_one_launch"] else [(2, 3), (4, 5)])
+    if not plan["convert_in_w2"]:
+        launches.append((6, 7))
+    for a0, a1 in launches:
+        assert hip.elapsed_ms(ev[a0], ev[a1]) >= 0.0
+    for (_, a1), (b0, _) in zip(launches, launches[1:]):
+        assert hip.elapsed_ms(ev[a1], ev[b0]) >= 0.0
+    for e in ev:
+        hip.destroy(e)
 
 
 def test_layer_empty_batch(dev):

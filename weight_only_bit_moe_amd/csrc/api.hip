@@ -99,6 +99,9 @@ void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
     plan->max_tiles = (int)(P / bm + (E < P ? E : P));
     plan->w13_variant = decode ? 2 : 1;
     plan->w2_variant = decode ? 2 : 1;
+    plan->gemms_one_launch =
+        decode && wna16::decode_one_launch(q13.bits, q13.group, q2.bits, q2.group, H, I) ? 1 : 0;
+    plan->convert_in_w2 = decode && (size_t)T * H <= wna16::kFusedConvertMax ? 1 : 0;
 }
 
 // The prefill-shaped kernels address activations, their bias terms and one
@@ -268,31 +271,28 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, ev[0]))) !=
         MOE_WNA16_OK)
         return st;
-    // Small outputs: the last w2 workgroup to finish rounds the sum to BF16
-    // itself, which saves the convert launch.  The profiled entry keeps the
-    // separate convert so that every step has its own events.
+    // Small outputs: the last decode w2 workgroup of each column block rounds
+    // that block to BF16, which saves the convert launch.  Decode shapes whose
+    // projections share a format run both GEMMs in one launch.  The profiled
+    // entry launches the same kernels; a shared launch carries the first
+    // step's start event and the last step's stop event, and the events in
+    // between are not recorded.
     uint16_t *outb = static_cast<uint16_t *>(out);
-    const bool fuse = !events && d.variant2 == 2 && (size_t)T * H <= wna16::kFusedConvertMax;
-    // Decode shapes on the plain entry point: both GEMMs in one launch when
-    // the two projections share a format (the profiled entry keeps one
-    // launch per step).
-    hipError_t he = hipErrorNotSupported;
-    if (!events)
-        he = wna16::launch_decode(w13_packed, w13_scales, w2_packed, w2_scales, topk_w, d, ws,
-                                  stream, fuse ? outb : nullptr);
-    if (he != hipErrorNotSupported) {
-        if ((st = hip_status(he)) != MOE_WNA16_OK)
+    const bool fuse = plan.convert_in_w2 != 0;
+    if (plan.gemms_one_launch) {
+        if ((st = hip_status(wna16::launch_decode(
+                 w13_packed, w13_scales, w2_packed, w2_scales, topk_w, d, ws, stream,
+                 wna16::KernelEvents{ev[1].start, ev[2].stop}, fuse ? outb : nullptr))) !=
+            MOE_WNA16_OK)
             return st;
-        if (fuse)
-            return MOE_WNA16_OK;
-        return hip_status(wna16::launch_convert(ws.out_f32, outb, (size_t)T * H, stream, ev[3]));
+    } else {
+        if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
+            MOE_WNA16_OK)
+            return st;
+        if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream,
+                                              ev[2], fuse ? outb : nullptr))) != MOE_WNA16_OK)
+            return st;
     }
-    if ((st = hip_status(wna16::launch_w13(w13_packed, w13_scales, d, ws, stream, ev[1]))) !=
-        MOE_WNA16_OK)
-        return st;
-    if ((st = hip_status(wna16::launch_w2(w2_packed, w2_scales, topk_w, d, ws, stream, ev[2],
-                                          fuse ? outb : nullptr))) != MOE_WNA16_OK)
-        return st;
     if (fuse)
         return MOE_WNA16_OK;
     return hip_status(wna16::launch_convert(ws.out_f32, outb, (size_t)T * H, stream, ev[3]));

@@ -1780,37 +1780,60 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
 
 template <int BITS, int GS>
 static hipError_t decode_dispatch(const GemmArgs &a13, GemmArgs a2, int max_tiles,
-                                  hipStream_t stream)
+                                  hipStream_t stream, const KernelEvents &ev)
 {
     constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
     using S13 = Stream<BITS, GS, 2, D13, true, true>;
     using S2 = Stream<BITS, GS, 2, D2, false, true>;
-    if ((a13.K / S13::UK) % D13 != 0 || (a2.K / S2::UK) % D2 != 0)
-        return hipErrorNotSupported;
     const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
     a2.tile_target = nblk13;
     const size_t l13 = S13::lds_bytes(a13.K), l2 = S2::lds_bytes(a2.K);
     hipExtLaunchKernelGGL((decode_kernel<BITS, GS, D13, BITS, GS, D2>),
                           dim3((unsigned)(max_tiles * (nblk13 + nblk2))), dim3(S13::NTHREADS),
-                          (uint32_t)(l13 > l2 ? l13 : l2), stream, nullptr, nullptr, 0, a13, a2,
-                          max_tiles, nblk13, nblk2);
+                          (uint32_t)(l13 > l2 ? l13 : l2), stream, ev.start, ev.stop, 0, a13,
+                          a2, max_tiles, nblk13, nblk2);
     return hipGetLastError();
+}
+
+template <int BITS, int GS>
+static bool decode_fits(int H, int I)
+{
+    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
+    using S13 = Stream<BITS, GS, 2, D13, true, true>;
+    using S2 = Stream<BITS, GS, 2, D2, false, true>;
+    return (H / S13::UK) % D13 == 0 && (I / S2::UK) % D2 == 0;
+}
+
+bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I)
+{
+    if (bits13 != bits2 || g13 != g2)
+        return false;
+    switch (bits13 * 1000 + g13) {   // 2-bit g32: both bodies do not fit one kernel's registers
+    case 2064: return decode_fits<2, 64>(H, I);
+    case 2128: return decode_fits<2, 128>(H, I);
+    case 4032: return decode_fits<4, 32>(H, I);
+    case 4064: return decode_fits<4, 64>(H, I);
+    case 4128: return decode_fits<4, 128>(H, I);
+    default: return false;
+    }
 }
 
 hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t *w2,
                          const uint16_t *s2, const float *topk_w, const LayerDims &d,
-                         const Workspace &ws, hipStream_t stream, uint16_t *out_bf16)
+                         const Workspace &ws, hipStream_t stream, const KernelEvents &ev,
+                         uint16_t *out_bf16)
 {
-    if (d.variant13 != 2 || d.variant2 != 2 || d.bits13 != d.bits2 || d.g13 != d.g2)
+    if (d.variant13 != 2 || d.variant2 != 2 ||
+        !decode_one_launch(d.bits13, d.g13, d.bits2, d.g2, d.H, d.I))
         return hipErrorNotSupported;
     const GemmArgs a13 = w13_args(w13, s13, d, ws);
     const GemmArgs a2 = w2_args(w2, s2, topk_w, d, ws, out_bf16);
-    switch (d.bits13 * 1000 + d.g13) {   // 2-bit g32: both bodies do not fit one kernel's registers
-    case 2064: return decode_dispatch<2, 64>(a13, a2, d.max_tiles, stream);
-    case 2128: return decode_dispatch<2, 128>(a13, a2, d.max_tiles, stream);
-    case 4032: return decode_dispatch<4, 32>(a13, a2, d.max_tiles, stream);
-    case 4064: return decode_dispatch<4, 64>(a13, a2, d.max_tiles, stream);
-    case 4128: return decode_dispatch<4, 128>(a13, a2, d.max_tiles, stream);
+    switch (d.bits13 * 1000 + d.g13) {
+    case 2064: return decode_dispatch<2, 64>(a13, a2, d.max_tiles, stream, ev);
+    case 2128: return decode_dispatch<2, 128>(a13, a2, d.max_tiles, stream, ev);
+    case 4032: return decode_dispatch<4, 32>(a13, a2, d.max_tiles, stream, ev);
+    case 4064: return decode_dispatch<4, 64>(a13, a2, d.max_tiles, stream, ev);
+    case 4128: return decode_dispatch<4, 128>(a13, a2, d.max_tiles, stream, ev);
     default: return hipErrorNotSupported;
     }
 }

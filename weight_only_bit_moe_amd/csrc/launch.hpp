@@ -60,7 +60,10 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
 // not allow it.  out_bf16 as for launch_w2.
 hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t *w2,
                          const uint16_t *s2, const float *topk_w, const LayerDims &d,
-                         const Workspace &ws, hipStream_t stream, uint16_t *out_bf16);
+                         const Workspace &ws, hipStream_t stream, const KernelEvents &ev,
+                         uint16_t *out_bf16);
+// Whether decode-shaped w13 and w2 of these formats and sizes run as one launch.
+bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I);
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
