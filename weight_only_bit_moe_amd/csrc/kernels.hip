@@ -700,6 +700,9 @@ struct Tile {
         const int g = cx.g, c = cx.lane & 15;
         const unsigned char *st = lds + stage * STAGE;
         const unsigned char *bw = st + B_OFF + cx.wave * B_WAVE;
+        // all code reads first (the copies below are ordered asm statements
+        // the compiler does not move reads across), then the unpack
+        uint32_t q[NT][GPC][NDW];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             const int row = j * 16 + c;
@@ -708,24 +711,28 @@ struct Tile {
                 const int off = CodeTraits<BITS, GS>::dword_off(G, g) * 4;   // inside the row's chunk
                 const unsigned char *src =
                     bw + row * RB + (((off >> 4) ^ swz(row)) << 4) + (off & 15);
-                uint32_t q[NDW];
                 if constexpr (NDW == 4) {
                     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src);
-                    q[0] = v[0];
-                    q[1] = v[1];
-                    q[2] = v[2];
-                    q[3] = v[3];
+                    q[j][G][0] = v[0];
+                    q[j][G][1] = v[1];
+                    q[j][G][2] = v[2];
+                    q[j][G][3] = v[3];
                 } else if constexpr (NDW == 2) {
                     const u32x2_t v = *reinterpret_cast<const u32x2_t *>(src);
-                    q[0] = v[0];
-                    q[1] = v[1];
+                    q[j][G][0] = v[0];
+                    q[j][G][1] = v[1];
                 } else {
-                    q[0] = *reinterpret_cast<const uint32_t *>(src);
+                    q[j][G][0] = *reinterpret_cast<const uint32_t *>(src);
                 }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+#pragma unroll
+            for (int G = 0; G < GPC; ++G)
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    bf[j][G * S + s] = unpack<BITS, GS, NDW>(q, s, g, magic);
-            }
+                    bf[j][G * S + s] = unpack<BITS, GS, NDW>(q[j][G], s, g, magic);
             copy_items<MTA>(C0 + j * (C1 - C0) / NT, C0 + (j + 1) * (C1 - C0) / NT, cx, pc);
         }
         load_subtile(st, cx, 0, af, nb);
