@@ -294,3 +294,149 @@ int oracle_align(const int32_t *ids, int T, int topk, int E, int block_m, int32_
     free(fill);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Quantizer: from float weights to the codes and scales the layer reads
+ * (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "How it was created"
+ * steps 2-5: symmetric b-bit weights per K group, a scale search weighted by
+ * an activation importance matrix, signed codes packed into 32-bit words, and
+ * weighted and unweighted reconstruction error; "imatrix-weighted RTN").
+ *
+ * Readings (the card names the steps, not the arithmetic):
+ *   Q1 the input is W [rows][K] in BF16 and an importance imp[K] >= 0 per
+ *      input channel (NULL: every channel 1, i.e. plain unweighted RTN).
+ *   Q2 base scale of a group: s0 = amax / ((2^b - 1) / 2) in FP32, amax the
+ *      largest |w| of the group (the group's range onto the code span).
+ *   Q3 candidates c = 0..C-1: s_c = fp16_rne(min(s0 * (1 - c / (2C)), 65504)),
+ *      each factor and product in FP32 (C = 1: s0 only).
+ *   Q4 codes for a scale s: q = clamp(rne(w / s), -2^(b-1), 2^(b-1) - 1) with
+ *      w / s an FP32 division; s = 0 gives q = 0.
+ *   Q5 err_c = sum_k imp_k (w_k - s_c q_k)^2 in double, ascending k; the
+ *      smallest err_c wins, ties to the smaller c.
+ *   Q6 error sums over the matrix (double): (w - w')^2, w^2, imp (w - w')^2,
+ *      imp w^2, with w' = s q the reconstruction.
+ * Codes are stored by R2/R3 (u = q + 2^(b-1), least-significant field first).
+ * ------------------------------------------------------------------------- */
+
+/* IEEE binary16 bits of the round-to-nearest-even of a finite v >= 0 that
+ * is at most 65504 (the largest finite half). */
+uint16_t oracle_f64_to_f16_rne(double v)
+{
+    if (v == 0.0)
+        return 0;
+    int e;
+    frexp(v, &e);                       /* v = f * 2^e, f in [0.5, 1) */
+    int ex = e - 1;                     /* floor(log2 v) */
+    if (ex < -14)
+        ex = -14;                       /* subnormal range: quantum 2^-24 */
+    double quantum = ldexp(1.0, ex - 10);
+    double r = rint(v / quantum) * quantum;   /* rint: nearest, ties to even */
+    if (r == 0.0)
+        return 0;
+    frexp(r, &e);
+    ex = e - 1;
+    if (ex < -14)                       /* subnormal: r = m * 2^-24 */
+        return (uint16_t)(r / ldexp(1.0, -24));
+    uint16_t frac = (uint16_t)(r / ldexp(1.0, ex - 10) - 1024.0);
+    return (uint16_t)(((ex + 15) << 10) | frac);
+}
+
+/* Q4: the code of w for the FP16 scale s (both exact in float). */
+static int quant_code(float w, float s, int bits)
+{
+    const int lo = -(1 << (bits - 1)), hi = (1 << (bits - 1)) - 1;
+    if (s == 0.0f)
+        return 0;
+    float r = rintf(w / s);
+    if (r < (float)lo)
+        return lo;
+    if (r > (float)hi)
+        return hi;
+    return (int)r;
+}
+
+/*
+ * Quantize W [rows][K] (BF16 bits) with groups of `group` along K.
+ * Writes codes [rows][K*bits/32], scales [rows][K/group] (FP16 bits),
+ * choice[rows][K/group] (the winning candidate c) and sums[4] (Q6).
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_quantize(const uint16_t *w, const float *imp, int rows, int K, int bits, int group,
+                    int ncand, uint32_t *codes, uint16_t *scales, int32_t *choice,
+                    double *sums)
+{
+    if (rows < 0 || K <= 0 || (bits != 2 && bits != 4) || group <= 0 || K % group ||
+        (K * bits) % 32 || ncand < 1)
+        return -1;
+    const int ngroups = K / group, kw = K * bits / 32, per_word = 32 / bits;
+    const float half_span = (float)((1 << bits) - 1) / 2.0f;
+    double s_err = 0.0, s_w2 = 0.0, s_ierr = 0.0, s_iw2 = 0.0;
+    int *q = (int *)malloc(sizeof(int) * (size_t)group);
+    int *qbest = (int *)malloc(sizeof(int) * (size_t)group);
+    if (!q || !qbest) {
+        free(q);
+        free(qbest);
+        return -1;
+    }
+    for (int n = 0; n < rows; ++n) {
+        uint32_t *row_words = codes + (size_t)n * kw;
+        memset(row_words, 0, sizeof(uint32_t) * (size_t)kw);
+        for (int G = 0; G < ngroups; ++G) {
+            const uint16_t *wg = w + (size_t)n * K + (size_t)G * group;
+            float amax = 0.0f;
+            for (int i = 0; i < group; ++i) {
+                float a = (float)fabs(oracle_bf16_to_f64(wg[i]));
+                if (a > amax)
+                    amax = a;
+            }
+            const float s0 = amax / half_span;                          /* Q2 */
+            double best = 0.0;
+            int cbest = -1;
+            uint16_t hbest = 0;
+            for (int c = 0; c < ncand; ++c) {
+                const float f = 1.0f - (float)c / (float)(2 * ncand);    /* Q3 */
+                float sc = s0 * f;
+                if (sc > 65504.0f)
+                    sc = 65504.0f;
+                const uint16_t h = oracle_f64_to_f16_rne((double)sc);
+                const double s = oracle_f16_to_f64(h);
+                double err = 0.0;
+                for (int i = 0; i < group; ++i) {
+                    const double wv = oracle_bf16_to_f64(wg[i]);
+                    q[i] = quant_code((float)wv, (float)s, bits);        /* Q4 */
+                    const double d = wv - s * (double)q[i];
+                    err += (imp ? (double)imp[G * group + i] : 1.0) * d * d;   /* Q5 */
+                }
+                if (cbest < 0 || err < best) {
+                    best = err;
+                    cbest = c;
+                    hbest = h;
+                    memcpy(qbest, q, sizeof(int) * (size_t)group);
+                }
+            }
+            scales[(size_t)n * ngroups + G] = hbest;
+            if (choice)
+                choice[(size_t)n * ngroups + G] = cbest;
+            const double s = oracle_f16_to_f64(hbest);
+            for (int i = 0; i < group; ++i) {
+                const int k = G * group + i;
+                const uint32_t u = (uint32_t)(qbest[i] + (1 << (bits - 1)));   /* R3 */
+                row_words[k / per_word] |= u << ((k % per_word) * bits);      /* R2 */
+                const double wv = oracle_bf16_to_f64(wg[i]);
+                const double d = wv - s * (double)qbest[i];
+                const double im = imp ? (double)imp[k] : 1.0;
+                s_err += d * d;                                              /* Q6 */
+                s_w2 += wv * wv;
+                s_ierr += im * d * d;
+                s_iw2 += im * wv * wv;
+            }
+        }
+    }
+    sums[0] = s_err;
+    sums[1] = s_w2;
+    sums[2] = s_ierr;
+    sums[3] = s_iw2;
+    free(q);
+    free(qbest);
+    return 0;
+}

@@ -61,6 +61,10 @@ def _load():
         lib.oracle_moe_forward_tokens.restype = i
         lib.oracle_align.argtypes = [P, i, i, i, i, P, P, P, P, P, P]
         lib.oracle_align.restype = i
+        lib.oracle_f64_to_f16_rne.argtypes = [d]
+        lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
+        lib.oracle_quantize.argtypes = [P, P, i, i, i, i, i, P, P, P, P]
+        lib.oracle_quantize.restype = i
         _lib = lib
     return _lib
 
@@ -180,3 +184,28 @@ def align(topk_ids, E: int, block_m: int):
     return dict(sorted_ids=sorted_ids[: n * block_m].copy(), tile_expert=tile_expert[:n].copy(),
                 expert_offsets=offsets, inv_perm=inv_perm[:P].copy(), num_tiles=n,
                 bad_ids=int(bad[0]))
+
+
+def f64_to_f16_rne(v: float) -> int:
+    """IEEE binary16 bits of round-to-nearest-even(v), 0 <= v <= 65504."""
+    return int(_load().oracle_f64_to_f16_rne(float(v)))
+
+
+def quantize(w_bf16, bits: int, group: int, ncand: int = 1, imp=None):
+    """Symmetric b-bit quantization of W [rows][K] given as BF16 bit patterns
+    (uint16), with the importance-weighted scale search of oracle_quantize.
+    Returns dict(codes [rows][K*bits/32] uint32, scales [rows][K/group] uint16
+    FP16 bits, choice [rows][K/group] int32, sums [4] float64)."""
+    w = _c(w_bf16, np.uint16)
+    rows, K = w.shape
+    codes = np.zeros((rows, K * bits // 32), np.uint32)
+    scales = np.zeros((rows, K // group), np.uint16)
+    choice = np.zeros((rows, K // group), np.int32)
+    sums = np.zeros(4, np.float64)
+    impa = None if imp is None else _c(imp, np.float32)
+    rc = _load().oracle_quantize(_ptr(w), None if impa is None else _ptr(impa), rows, K, bits,
+                                 group, ncand, _ptr(codes), _ptr(scales), _ptr(choice),
+                                 _ptr(sums))
+    if rc != 0:
+        raise ValueError("oracle_quantize rejected its arguments")
+    return dict(codes=codes, scales=scales, choice=choice, sums=sums)
