@@ -51,6 +51,8 @@ def parse():
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=None,
                     help="rocprofv3 counter summary holding the dominant kernel's HBM traffic")
+    ap.add_argument("--quantize", action="store_true",
+                    help="measure the quantizer instead of the layer (its own JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times) "
                          "and exit: the reference reading for HBM byte counters")
@@ -79,6 +81,11 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def event(self):
         e = ctypes.c_void_p()
@@ -125,6 +132,9 @@ def main():
         print("bench.py measures one GPU: this layer has no multi-GPU path here "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.quantize:
+        bench_quantize(args)
+        return
 
     import numpy as np
     import torch
@@ -297,6 +307,149 @@ def main():
         for h in e:
             hip.destroy(h)
     print(json.dumps(result), flush=True)
+
+
+# Lane operations per (weight, candidate) of the quantizer's definition: the
+# division, the rounding, two clamp comparisons, s*q, the subtraction, two
+# multiplications by imp and d, and the addition into the group's error.
+QUANT_OPS_PER_EVAL = 9
+# One VALU lane operation per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def bench_quantize(args):
+    """All routed experts of one layer quantized on the GPU (2-bit, group 128,
+    16-candidate importance-weighted scale search): the fused gate/up matrices
+    [256*4096, 4096] and the down matrices [256*4096, 2048]."""
+    import numpy as np
+    import torch
+
+    import weight_only_bit_moe_amd as M
+    from weight_only_bit_moe_amd.inputs import (QUANT_WORKLOAD, make_dense_weights_device,
+                                                make_importance)
+
+    if not os.path.exists(M.LIB_PATH):
+        from weight_only_bit_moe_amd import build as hip_build
+        hip_build.build()
+    steps = args.steps if args.steps is not None else 10
+    warmup = args.warmup if args.warmup is not None else 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ops = []
+    for j, sp in enumerate(QUANT_WORKLOAD):
+        w = make_dense_weights_device(sp.rows, sp.K, 1000 + j, dev, sp.w_std)
+        imp = torch.from_numpy(make_importance(sp.K, 2000 + j, sp.imp_sigma, sp.outlier_frac,
+                                               sp.outlier_mult)).to(dev)
+        codes = torch.empty((sp.rows, sp.K * sp.bits // 32), dtype=torch.int32, device=dev)
+        scales = torch.empty((sp.rows, sp.K // sp.group), dtype=torch.float16, device=dev)
+        sums = torch.empty(4, dtype=torch.float64, device=dev)
+        ops.append((sp, w, imp, codes, scales, sums))
+    torch.cuda.synchronize(dev)
+
+    def call(sp, w, imp, codes, scales, sums):
+        st = M.moe_wna16_quantize(w.data_ptr(), imp.data_ptr(), sp.rows, sp.K,
+                                  (sp.bits, sp.group), sp.ncand, codes.data_ptr(),
+                                  scales.data_ptr(), sums.data_ptr(), stream)
+        if st != 0:
+            raise M.MoeWna16Error(st, "moe_wna16_quantize")
+
+    hip = Hip()
+    evs = [[(hip.event(), hip.event()) for _ in ops] for _ in range(steps)]
+    for _ in range(warmup):
+        for o in ops:
+            call(*o)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for j, o in enumerate(ops):
+            hip.record(evs[i][j][0], stream)
+            call(*o)
+            hip.record(evs[i][j][1], stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    call_ms = [float(np.mean([hip.elapsed_ms(*evs[i][j]) for i in range(steps)]))
+               for j in range(len(ops))]
+    for row in evs:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
+
+    n_weights = sum(sp.rows * sp.K for sp, *_ in ops)
+    j = int(np.argmax(call_ms))
+    sp = ops[j][0]
+    evals = sp.rows * sp.K * sp.ncand
+    achieved = QUANT_OPS_PER_EVAL * evals / (call_ms[j] * 1e-3) / 1e12
+    hbm_bytes = sp.rows * sp.K * (2 + sp.bits / 8) + sp.rows * (sp.K // sp.group) * 2
+    roof = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "Top/s",
+            "frac": achieved / ALU_PEAK_TOPS, "traffic": None,
+            "kernel": "quantize_kernel (" + sp.name + ")", "kernel_ms": call_ms[j],
+            "algorithmic_ops": QUANT_OPS_PER_EVAL * evals,
+            "hbm_gbs": hbm_bytes / (call_ms[j] * 1e-3) / 1e9}
+
+    # weighted reconstruction error of the search against plain RTN (one
+    # candidate) on 24 single-expert matrices: 12 experts' gate/up and down
+    red = []
+    for e in range(12):
+        for sp_, w, imp, codes, scales, sums in ops:
+            rows = sp_.rows // 256
+            sub = w[e * rows:(e + 1) * rows]
+            r1 = M.quantize(sub, sp_.bits, sp_.group, 1, imp)["sums"]
+            rc = M.quantize(sub, sp_.bits, sp_.group, sp_.ncand, imp)["sums"]
+            red.append(1.0 - float(rc[2]) / float(r1[2]))
+    result = {
+        "metric": "routed-expert weights quantized per second on 1 MI355X",
+        "value": n_weights / (ms_per_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+f64",
+        "data": "synthetic (seeded Student-t weights, lognormal importance with 1% hot channels)",
+        "config": {"workload": "quantize-E256-H4096-I2048-w2g128-C16",
+                   "matrices": [f"{sp_.name}: [{sp_.rows}, {sp_.K}]" for sp_, *_ in ops],
+                   "bits": sp.bits, "group": sp.group, "candidates": sp.ncand,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "call_ms": call_ms,
+        "weighted_error_reduction_vs_rtn": {
+            "median": float(np.median(red)), "min": float(np.min(red)),
+            "max": float(np.max(red)), "matrices": len(red)},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_quantize(ops[0], args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_quantize(op, budget_s):
+    """The CPU oracle's quantizer (single thread, float64 errors) on leading
+    rows of the first matrix, as many as fit the time budget."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle
+
+    sp, w, imp, *_ = op
+    imp_h = imp.cpu().numpy()
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.quantize(w[:rows].view(torch.int16).cpu().numpy().view(np.uint16), sp.bits, sp.group,
+                    sp.ncand, imp_h)
+    per_row = (time.perf_counter() - t0) / rows
+    rows = int(max(rows, min(sp.rows, budget_s / max(per_row, 1e-9))))
+    wh = w[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    oracle.quantize(wh, sp.bits, sp.group, sp.ncand, imp_h)
+    el = time.perf_counter() - t0
+    return {"value": rows * sp.K / el, "unit": "weights/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {sp.rows} rows of {sp.name}, {el:.1f} s"}
 
 
 def cpu_baseline(L, budget_s):

@@ -179,6 +179,36 @@ int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m
  */
 int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t *offset_out);
 
+/*
+ * Quantizer: float weights -> the packed codes and scales the layer reads
+ * (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "How it was created"
+ * steps 2-5).  For every row and every group of `q.group` consecutive K
+ * elements, with amax the group's largest |w|:
+ *   s0  = amax / ((2^b - 1) / 2)                            (FP32)
+ *   s_c = fp16_rne(min(s0 * (1 - c / (2C)), 65504)),  c = 0 .. C-1
+ *   q   = clamp(rne(w / s_c), -2^(b-1), 2^(b-1) - 1)         (FP32 division; 0 if s_c = 0)
+ *   err_c = sum over the group of imp[k] * (w - s_c * q)^2   (FP64)
+ * and the smallest err_c wins (ties to the smaller c); C = n_candidates, so
+ * C = 1 is plain round-to-nearest with the absmax scale.
+ *
+ *   w           [rows, K] bf16, row-major                        4-byte aligned
+ *   imp         [K] float32 importance per input channel (>= 0), or NULL for
+ *               all ones (the unweighted search)                 4-byte aligned
+ *   codes_out   [rows, K*b/32] int32 in the packed format above  4-byte aligned
+ *   scales_out  [rows, K/group] fp16                             2-byte aligned
+ *   err_sums_out [4] float64, overwritten: sum (w - w')^2, sum w^2,
+ *               sum imp (w - w')^2, sum imp w^2 over the matrix, w' the
+ *               dequantized weight (summation order unspecified) 8-byte aligned
+ *
+ * rows >= 0 (rows = 0 writes zero sums), K > 0 a multiple of the group;
+ * 1 <= n_candidates <= 64 (offsets are 64-bit: no limit on rows * K).  Non-finite weights are not
+ * checked (their groups' codes are unspecified).  An imp containing NaN or
+ * negative values gives unspecified scale choices.
+ */
+int moe_wna16_quantize(const void *w, const float *imp, int rows, int K, moe_wna16_qparams q,
+                       int n_candidates, int32_t *codes_out, uint16_t *scales_out,
+                       double *err_sums_out, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *moe_wna16_status_string(int status);
 

@@ -139,3 +139,30 @@ def test_library_carries_gfx950_code_only(lib):
     assert b"gfx950" in blob
     for other in (b"gfx942", b"gfx90a", b"gfx1100"):
         assert other not in blob
+
+
+def test_quantize_rejects(lib):
+    f = M.moe_wna16_quantize
+    ok = dict(w=256, imp=None, rows=4, K=256, q=(4, 128), n_candidates=8, codes_out=256,
+              scales_out=256, err_sums_out=256, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["w"], a["imp"], a["rows"], a["K"], a["q"], a["n_candidates"],
+                 a["codes_out"], a["scales_out"], a["err_sums_out"], a["stream"])
+
+    assert call(rows=-1) == Bd.EINVAL
+    assert call(K=0) == Bd.EINVAL
+    assert call(n_candidates=0) == Bd.EINVAL
+    assert call(n_candidates=65) == Bd.EINVAL
+    assert call(q=(3, 128)) == Bd.EUNSUPPORTED
+    assert call(q=(4, 96)) == Bd.EUNSUPPORTED
+    assert call(K=192) == Bd.EUNSUPPORTED          # not a multiple of the group
+    assert call(w=0) == Bd.EINVAL
+    assert call(err_sums_out=0) == Bd.EINVAL
+    assert call(w=258) == Bd.EALIGN
+    assert call(imp=258) == Bd.EALIGN
+    assert call(err_sums_out=260) == Bd.EALIGN
+    assert call(scales_out=257) == Bd.EALIGN
+    # an empty matrix needs no weight, code or scale buffer
+    assert call(rows=0, w=0, codes_out=0, scales_out=0) in (Bd.EHIP, Bd.EARCH, Bd.OK)

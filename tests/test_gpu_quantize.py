@@ -1,0 +1,188 @@
+"""GPU parity of the quantizer (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16",
+"How it was created" steps 2-5) against the CPU oracle, through the C ABI.
+
+What is unique is compared bit for bit: the FP16 scale of every group whose
+scale choice the two sides agree on, and then every code word of that group.
+The search compares FP64 error sums that the two sides add up in different
+orders, so two candidates whose errors agree to ~1e-16 may be ranked either
+way; for such groups the GPU's choice is checked to be valid instead (its
+codes are the rounded, clamped w / s of its own scale, and its weighted error
+equals the oracle's minimum to 1e-12 relative).  The four error sums agree to
+1e-9 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import weight_only_bit_moe_amd as M
+from oracle import oracle as O
+from tests import _gpu as G
+from weight_only_bit_moe_amd.inputs import (QUANT_WORKLOAD, bf16_bits_to_f32,
+                                            make_dense_weights, make_dense_weights_device,
+                                            make_importance)
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(2, 32), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128)]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return G.device()
+
+
+def gpu_quantize(w_bits, bits, group, ncand, imp, dev):
+    w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    it = None if imp is None else torch.from_numpy(np.ascontiguousarray(imp, np.float32)).to(dev)
+    r = M.quantize(w, bits, group, ncand, it)
+    torch.cuda.synchronize(dev)
+    return dict(codes=r["codes"].cpu().numpy().view(np.uint32),
+                scales=r["scales"].cpu().numpy().view(np.uint16),
+                sums=r["sums"].cpu().numpy())
+
+
+def group_error(w_row, words_row, scales_row, K, bits, group, imp, g):
+    """Weighted squared error of group g of one row, decoded with the oracle's
+    field decoder."""
+    q = O.codes(words_row, K, bits)[g * group:(g + 1) * group].astype(np.float64)
+    s = O.f16_to_f64(int(scales_row[g]))
+    wv = bf16_bits_to_f32(w_row[g * group:(g + 1) * group]).astype(np.float64)
+    im = np.ones(group) if imp is None else imp[g * group:(g + 1) * group].astype(np.float64)
+    return float((im * (wv - s * q) ** 2).sum()), q, s, wv
+
+
+def assert_quant_parity(w_bits, bits, group, ncand, imp, got, ref, max_ties=None):
+    rows, K = w_bits.shape
+    ng = K // group
+    pf = 32 // bits
+    diff = got["scales"] != ref["scales"]                       # [rows, ng]
+    n_diff = int(diff.sum())
+    limit = max(2, rows * ng // 1000) if max_ties is None else max_ties
+    assert n_diff <= limit, f"{n_diff} of {rows * ng} group scales differ"
+    # code words of the agreeing groups: bit for bit
+    word_group = (np.arange(K // pf) * pf) // group
+    same_w = ~diff[:, word_group]
+    np.testing.assert_array_equal(got["codes"][same_w], ref["codes"][same_w])
+    # the groups ranked differently: a near-tie, and valid codes for the GPU's scale
+    for r, g in zip(*np.nonzero(diff)):
+        e_gpu, q_gpu, s_gpu, wv = group_error(w_bits[r], got["codes"][r], got["scales"][r], K,
+                                              bits, group, imp, g)
+        e_ref = group_error(w_bits[r], ref["codes"][r], ref["scales"][r], K, bits, group, imp,
+                            g)[0]
+        assert abs(e_gpu - e_ref) <= 1e-12 * max(e_ref, 1e-300), (r, g, e_gpu, e_ref)
+        lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+        with np.errstate(divide="ignore", invalid="ignore"):
+            expect = np.clip(np.rint(wv.astype(np.float32) / np.float32(s_gpu)), lo, hi)
+        if s_gpu == 0:
+            expect = np.zeros_like(expect)
+        np.testing.assert_array_equal(q_gpu, expect)
+    np.testing.assert_allclose(got["sums"], ref["sums"], rtol=1e-9, atol=0)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("ncand", [1, 7, 16])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_quantize_matches_oracle(dev, bits, group, ncand, weighted):
+    """37 rows x 2304 columns: two full 1024-column strips and a ragged third."""
+    rows, K = 37, 2304
+    seed = bits * 100 + group + ncand
+    w = make_dense_weights(rows, K, seed)
+    imp = make_importance(K, seed + 1) if weighted else None
+    got = gpu_quantize(w, bits, group, ncand, imp, dev)
+    ref = O.quantize(w, bits, group, ncand, imp)
+    assert_quant_parity(w, bits, group, ncand, imp, got, ref)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 128), (4, 32)])
+def test_quantize_many_rows_per_wave(dev, bits, group):
+    """More rows than waves per strip, so every wave walks several rows
+    (1152 columns: one full strip and one of 128 columns)."""
+    rows, K = 6000, 1152
+    w = make_dense_weights(rows, K, 11 + bits)
+    imp = make_importance(K, 12)
+    got = gpu_quantize(w, bits, group, 8, imp, dev)
+    ref = O.quantize(w, bits, group, 8, imp)
+    assert_quant_parity(w, bits, group, 8, imp, got, ref)
+
+
+def bf16_exact(v):
+    f = np.asarray(v, np.float32)
+    b = f.view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0)
+    return (b >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (4, 64)])
+def test_quantize_special_groups(dev, bits, group):
+    """Zero groups (scale 0, every field at its bias), groups whose scale
+    underflows FP16 to zero, groups that saturate the FP16 scale, exact
+    half-way quotients (round half to even), signed zeros and a single
+    non-zero weight."""
+    K = 4 * group
+    rng = np.random.default_rng(bits + group)
+    rows = []
+    rows.append(np.zeros(K))
+    rows.append(np.full(K, -0.0))
+    tiny = np.zeros(K)
+    tiny[::3] = 2.0 ** -30                                    # s0 far below FP16's range
+    rows.append(tiny)
+    big = rng.integers(-3, 4, size=K) * 2.0 ** 20             # s0 above 65504
+    rows.append(big)
+    # w = (m + 1/2) * 2^j for small m: quotients that are exact half-integers
+    # (with amax = (2^b - 1)/2 * 2^-6 the first candidate's scale is 2^-6)
+    half = (rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), size=K) + 0.5) * 2.0 ** -6
+    half[::group] = ((1 << bits) - 1) / 2 * 2.0 ** -6
+    rows.append(half)
+    one = np.zeros(K)
+    one[group + 5] = -0.375
+    rows.append(one)
+    w = bf16_exact(np.stack(rows).astype(np.float32))
+    for ncand in (1, 5):
+        for imp in (None, make_importance(K, 3)):
+            got = gpu_quantize(w, bits, group, ncand, imp, dev)
+            ref = O.quantize(w, bits, group, ncand, imp)
+            assert_quant_parity(w, bits, group, ncand, imp, got, ref, max_ties=0)
+
+
+def test_quantize_empty_matrix_writes_zero_sums(dev):
+    w = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    r = M.quantize(w, 4, 128, 4)
+    torch.cuda.synchronize(dev)
+    assert r["codes"].shape == (0, 32)
+    assert r["sums"].cpu().tolist() == [0.0, 0.0, 0.0, 0.0]
+
+
+def test_quantize_overwrites_sums_between_calls(dev):
+    """The error sums are overwritten, not accumulated, by each call."""
+    w = make_dense_weights(16, 512, 9)
+    a = gpu_quantize(w, 4, 128, 4, None, dev)
+    b = gpu_quantize(w, 4, 128, 4, None, dev)
+    assert np.array_equal(a["sums"], b["sums"])
+    np.testing.assert_allclose(a["sums"], O.quantize(w, 4, 128, 4)["sums"], rtol=1e-9)
+
+
+@pytest.mark.parametrize("spec", QUANT_WORKLOAD, ids=lambda s: s.name)
+def test_quantize_full_workload_sampled_rows(dev, spec):
+    """The benchmark's operands (all routed experts of one layer), in the same
+    launch: rows sampled across the matrix are checked against the oracle."""
+    w = make_dense_weights_device(spec.rows, spec.K, 1234, dev, spec.w_std)
+    imp = make_importance(spec.K, 99, spec.imp_sigma, spec.outlier_frac, spec.outlier_mult)
+    r = M.quantize(w, spec.bits, spec.group, spec.ncand,
+                   torch.from_numpy(imp).to(dev))
+    torch.cuda.synchronize(dev)
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, spec.rows - 1],
+                                       rng.integers(0, spec.rows, size=62)]))
+    idx = torch.from_numpy(sample).to(dev)
+    w_s = w.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    got = dict(codes=r["codes"].index_select(0, idx).cpu().numpy().view(np.uint32),
+               scales=r["scales"].index_select(0, idx).cpu().numpy().view(np.uint16))
+    ref = O.quantize(w_s, spec.bits, spec.group, spec.ncand, imp)
+    got["sums"] = ref["sums"]          # sums cover the whole matrix; checked below
+    assert_quant_parity(w_s, spec.bits, spec.group, spec.ncand, imp, got, ref)
+    # whole-matrix sums: sum w^2 against torch's FP64 sum, the rest by their order
+    sums = r["sums"].cpu().numpy()
+    assert np.all(np.isfinite(sums)) and np.all(sums >= 0)
+    assert sums[0] < sums[1] and sums[2] < sums[3]
+    w2 = sum(float((w[i:i + 65536].double() ** 2).sum()) for i in range(0, spec.rows, 65536))
+    np.testing.assert_allclose(sums[1], w2, rtol=1e-9)

@@ -62,3 +62,18 @@ def test_outlier_channels():
 def test_named_configs_shapes():
     assert CONFIGS[2].T == 4 and CONFIGS[2].bits13 == 2 and CONFIGS[5].group2 == 64
     assert CONFIGS[4].clamp == 7.0 and CONFIGS[5].x_sigma == 2.0
+
+
+def test_dense_weights_and_importance_recipe():
+    from weight_only_bit_moe_amd.inputs import make_dense_weights, make_importance
+    w = make_dense_weights(64, 1024, 5)
+    assert w.dtype == np.uint16 and w.shape == (64, 1024)
+    assert np.array_equal(w, make_dense_weights(64, 1024, 5))
+    f = bf16_bits_to_f32(w).astype(np.float64)
+    # t4 * 0.02: variance df/(df-2) * 0.02^2 = 8e-4; heavy tails (kurtosis > normal's 3)
+    assert abs(f.var() / 8e-4 - 1) < 0.15
+    assert ((f - f.mean()) ** 4).mean() / f.var() ** 2 > 4.0
+    imp = make_importance(4096, 7)
+    assert imp.dtype == np.float32 and imp.shape == (4096,) and np.all(imp > 0)
+    assert np.sum(imp > 30) >= 30            # about 1% outlier channels at 100x
+    assert np.array_equal(imp, make_importance(4096, 7))

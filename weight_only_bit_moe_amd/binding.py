@@ -20,7 +20,7 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP = 0, -1, -2, -3, -4, -
 #: every symbol include/moe_wna16.h declares
 EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset", "moe_wna16_plan",
             "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_align",
-            "moe_wna16_status_string")
+            "moe_wna16_quantize", "moe_wna16_status_string")
 
 
 class QParams(ctypes.Structure):
@@ -67,6 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_wna16_forward_profiled.restype = i
     lib.moe_wna16_align.argtypes = [P, i, i, i, i, P, P, P, P, P, P, P]
     lib.moe_wna16_align.restype = i
+    lib.moe_wna16_quantize.argtypes = [P, P, i, i, QParams, i, P, P, P, P]
+    lib.moe_wna16_quantize.restype = i
     lib.moe_wna16_status_string.argtypes = [i]
     lib.moe_wna16_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -137,6 +139,13 @@ def moe_wna16_align(topk_ids, T, topk, E, block_m, sorted_ids, tile_expert, expe
     """Raw entry point on integer device addresses; returns the status."""
     return load_library().moe_wna16_align(topk_ids, T, topk, E, block_m, sorted_ids, tile_expert,
                                           expert_offsets, inv_perm, num_tiles, bad_ids, stream)
+
+
+def moe_wna16_quantize(w, imp, rows, K, q: Tuple[int, int], n_candidates, codes_out,
+                       scales_out, err_sums_out, stream) -> int:
+    """Raw entry point on integer device addresses; returns the status."""
+    return load_library().moe_wna16_quantize(w, imp, rows, K, QParams(*q), n_candidates,
+                                             codes_out, scales_out, err_sums_out, stream)
 
 
 # ---- torch conveniences (allocation + marshalling) --------------------------
@@ -240,3 +249,29 @@ def align(topk_ids, E: int, block_m: int):
     if st != OK:
         raise MoeWna16Error(st, "moe_wna16_align")
     return r
+
+
+def quantize(w, bits: int, group: int, n_candidates: int = 1, imp=None):
+    """Quantize W [rows, K] (bf16, on the GPU) on the GPU.  Returns dict(codes
+    int32 [rows, K*bits/32], scales fp16 [rows, K/group], sums float64 [4]:
+    sum (w-w')^2, sum w^2, sum imp (w-w')^2, sum imp w^2)."""
+    torch = _torch()
+    dev = w.device
+    _check(w, "w", (torch.bfloat16,), dev)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, K]")
+    rows, K = w.shape
+    if imp is not None:
+        _check(imp, "imp", (torch.float32,), dev)
+        if imp.shape != (K,):
+            raise ValueError(f"imp must have shape ({K},)")
+    codes = torch.empty((rows, K * bits // 32), dtype=torch.int32, device=dev)
+    scales = torch.empty((rows, max(K // group, 1)), dtype=torch.float16, device=dev)
+    sums = torch.empty(4, dtype=torch.float64, device=dev)
+    st = moe_wna16_quantize(w.data_ptr() if rows else None,
+                            None if imp is None else imp.data_ptr(), rows, K, (bits, group),
+                            n_candidates, codes.data_ptr() if rows else None,
+                            scales.data_ptr() if rows else None, sums.data_ptr(), _stream(dev))
+    if st != OK:
+        raise MoeWna16Error(st, "moe_wna16_quantize")
+    return dict(codes=codes, scales=scales[:, :K // group], sums=sums)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_wna16.so")
-SOURCES = ["kernels.hip", "api.hip"]
+SOURCES = ["kernels.hip", "quantize.hip", "api.hip"]
 ARCH = "gfx950"
 
 
@@ -35,7 +35,7 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False, jobs: int = 2) -> str:
+def build(verbose: bool = False, jobs: int = 3) -> str:
     """Compile every source to an object in parallel, then link the library."""
     bdir = os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)

@@ -347,4 +347,25 @@ int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m
                                           expert_offsets, inv_perm, num_tiles, bad_ids, stream));
 }
 
+int moe_wna16_quantize(const void *w, const float *imp, int rows, int K, moe_wna16_qparams q,
+                       int n_candidates, int32_t *codes_out, uint16_t *scales_out,
+                       double *err_sums_out, hipStream_t stream)
+{
+    if (rows < 0 || K <= 0 || n_candidates < 1 || n_candidates > 64)
+        return MOE_WNA16_EINVAL;
+    if (!valid_qparams(q) || K % q.group)
+        return MOE_WNA16_EUNSUPPORTED;
+    if ((rows > 0 && (!w || !codes_out || !scales_out)) || !err_sums_out)
+        return MOE_WNA16_EINVAL;
+    if (!aligned(w, 4) || !aligned(imp, 4) || !aligned(codes_out, 4) ||
+        !aligned(scales_out, 2) || !aligned(err_sums_out, 8))
+        return MOE_WNA16_EALIGN;
+    const int st = check_device();
+    if (st != MOE_WNA16_OK)
+        return st;
+    return hip_status(wna16::launch_quantize(
+        static_cast<const uint16_t *>(w), imp, rows, K, q.bits, q.group, n_candidates,
+        reinterpret_cast<uint32_t *>(codes_out), scales_out, err_sums_out, stream));
+}
+
 }  // extern "C"

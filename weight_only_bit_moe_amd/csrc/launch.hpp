@@ -67,6 +67,11 @@ bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I);
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
+// Quantizer (quantize.hip): W [rows][K] BF16 -> codes, FP16 scales and the
+// four reconstruction error sums.
+hipError_t launch_quantize(const uint16_t *w, const float *imp, int rows, int K, int bits,
+                           int group, int ncand, uint32_t *codes, uint16_t *scales,
+                           double *sums, hipStream_t stream);
 // FP32 accumulator -> BF16 output (round to nearest even).
 hipError_t launch_convert(const float *src, uint16_t *dst, size_t n, hipStream_t stream,
                           const KernelEvents &ev);

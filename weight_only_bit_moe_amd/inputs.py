@@ -39,6 +39,11 @@ __all__ = [
     "make_config",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "QuantSpec",
+    "QUANT_WORKLOAD",
+    "make_dense_weights",
+    "make_dense_weights_device",
+    "make_importance",
 ]
 
 
@@ -231,3 +236,84 @@ CONFIGS = {
 def make_config(idx: int, seed: Optional[int] = None) -> Layer:
     """Layer of named workload `idx` (1..5); the seed defaults to `idx`."""
     return make_layer(CONFIGS[idx], idx if seed is None else seed)
+
+
+# ---- dense weights for the quantizer -----------------------------------------
+#
+# The quantizer's inputs (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16",
+# "How it was created": routed-expert matrices and an activation importance
+# vector per input channel).  The real matrices and importance data are not
+# available, so:
+#   weights    Student-t with 4 degrees of freedom times `w_std`, rounded to
+#              BF16 (heavy tails give groups with a few large weights, the case
+#              a scale search exists for).  t4 = z / sqrt(chi2_4 / 4) with
+#              chi2_4 = -2 ln(U1 U2).
+#   importance lognormal exp(sigma * z) per input channel, and a fraction
+#              `outlier_frac` of channels multiplied by outlier_mult^2 (the mean
+#              squared activation of a channel that runs outlier_mult times
+#              hotter).
+
+@dataclasses.dataclass(frozen=True)
+class QuantSpec:
+    """One quantizer workload: `matrices` of [rows, K] each."""
+
+    name: str
+    rows: int
+    K: int
+    bits: int
+    group: int
+    ncand: int
+    matrices: int = 1
+    w_std: float = 0.02
+    imp_sigma: float = 1.0
+    outlier_frac: float = 0.01
+    outlier_mult: float = 10.0
+
+
+#: All routed experts of one layer in the 2-bit, group-128 format: the fused
+#: gate/up matrices of 256 experts as one [256 * 4096, 4096] operand and the
+#: down matrices as one [256 * 4096, 2048] operand, with a 16-point scale search.
+QUANT_WORKLOAD = (
+    QuantSpec("quantize-w13-E256-w2g128-C16", rows=256 * 4096, K=4096, bits=2, group=128,
+              ncand=16),
+    QuantSpec("quantize-w2-E256-w2g128-C16", rows=256 * 4096, K=2048, bits=2, group=128,
+              ncand=16),
+)
+
+
+def make_dense_weights(rows: int, K: int, seed: int, w_std: float = 0.02) -> np.ndarray:
+    """Host draw: BF16 bit patterns [rows, K] of w_std * t4."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((rows, K))
+    u = rng.random((2, rows, K))
+    t = z / np.sqrt(-0.5 * np.log(u[0] * u[1] + 1e-300))
+    return f32_to_bf16_bits((t * w_std).astype(np.float32))
+
+
+def make_dense_weights_device(rows: int, K: int, seed: int, device, w_std: float = 0.02,
+                              chunk_rows: int = 1 << 15):
+    """Device draw of the same distribution (torch's generator, so other bytes
+    than the host draw): a BF16 tensor [rows, K] on `device`, made in chunks."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((rows, K), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        n = min(chunk_rows, rows - r0)
+        z = torch.randn((n, K), generator=g, device=device)
+        u = torch.rand((2, n, K), generator=g, device=device)
+        t = z / torch.sqrt(-0.5 * torch.log(u[0] * u[1] + 1e-30))
+        out[r0:r0 + n] = (t * w_std).to(torch.bfloat16)
+    return out
+
+
+def make_importance(K: int, seed: int, sigma: float = 1.0, outlier_frac: float = 0.01,
+                    outlier_mult: float = 10.0) -> np.ndarray:
+    """Importance per input channel, float32 [K], all > 0."""
+    rng = np.random.default_rng(seed)
+    imp = np.exp(sigma * rng.standard_normal(K))
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        imp[rng.choice(K, size=n_out, replace=False)] *= outlier_mult ** 2
+    return imp.astype(np.float32)
