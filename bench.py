@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 KERNEL_SOURCE = os.path.join(ROOT, "weight_only_bit_moe_amd", "csrc", "kernels.hip")
+QUANT_SOURCE = os.path.join(ROOT, "weight_only_bit_moe_amd", "csrc", "quantize.hip")
 
 
 def parse():
@@ -108,13 +109,13 @@ def per_expert_bytes(bits, group, rows, K):
     return rows * K * bits // 8 + rows * (K // group) * 2
 
 
-def kernel_traffic(path, kernel):
+def kernel_traffic(path, kernel, source=KERNEL_SOURCE):
     """HBM bytes per launch from a committed counter summary, or None when the
     summary is missing or was taken on a different kernel source."""
     if not path or not os.path.exists(path):
         return None
     text = open(path).read()
-    want = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    want = hashlib.sha256(open(source, "rb").read()).hexdigest()
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(rf"traffic_bytes_per_launch\[{re.escape(kernel)}\]:\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b or m_sha.group(1) != want:
@@ -382,8 +383,12 @@ def bench_quantize(args):
     evals = sp.rows * sp.K * sp.ncand
     achieved = QUANT_OPS_PER_EVAL * evals / (call_ms[j] * 1e-3) / 1e12
     hbm_bytes = sp.rows * sp.K * (2 + sp.bits / 8) + sp.rows * (sp.K // sp.group) * 2
+    workload = "quantize-E256-H4096-I2048-w2g128-C16"
+    traffic_file = args.traffic_file or os.path.join(ROOT, "profiles",
+                                                     f"counters_{workload}.md")
     roof = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "Top/s",
-            "frac": achieved / ALU_PEAK_TOPS, "traffic": None,
+            "frac": achieved / ALU_PEAK_TOPS,
+            "traffic": kernel_traffic(traffic_file, sp.name, QUANT_SOURCE),
             "kernel": "quantize_kernel (" + sp.name + ")", "kernel_ms": call_ms[j],
             "algorithmic_ops": QUANT_OPS_PER_EVAL * evals,
             "hbm_gbs": hbm_bytes / (call_ms[j] * 1e-3) / 1e9}
@@ -411,7 +416,7 @@ def bench_quantize(args):
         "vs_baseline": None,
         "dtype": "f32+f64",
         "data": "synthetic (seeded Student-t weights, lognormal importance with 1% hot channels)",
-        "config": {"workload": "quantize-E256-H4096-I2048-w2g128-C16",
+        "config": {"workload": workload,
                    "matrices": [f"{sp_.name}: [{sp_.rows}, {sp_.K}]" for sp_, *_ in ops],
                    "bits": sp.bits, "group": sp.group, "candidates": sp.ncand,
                    "parallelism": "none (1 GPU)"},
