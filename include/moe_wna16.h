@@ -209,6 +209,51 @@ int moe_wna16_quantize(const void *w, const float *imp, int rows, int K, moe_wna
                        int n_candidates, int32_t *codes_out, uint16_t *scales_out,
                        double *err_sums_out, hipStream_t stream);
 
+/*
+ * Prepared codes: a one-time reorder of one projection's packed codes into the
+ * order the decode-shaped kernels stream (a one-time setup step and an
+ * interface variant of the packed format of model card
+ * "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What changed").  A pure
+ * permutation of the 32-bit words:
+ *
+ *   a load unit is U = 512 / bits consecutive K elements of one row (16
+ *   words); a block is 16 rows x one unit (256 words); blocks are stored
+ *   [expert][row / 16][unit].  Inside a block, for rows r = 0..15 and lane
+ *   groups g = 0..3, slot (g * 16 + r) holds words 4 (g*16+r) .. +3: for each
+ *   quantization group of the unit in turn, the words of row r that hold the
+ *   codes at in-group K offsets [g * group / 4, (g + 1) * group / 4).  For
+ *   2-bit codes with group 32 (half a word per lane group and group), lane
+ *   groups 2h and 2h+1 share one slot: slot (h * 16 + r) holds words
+ *   8 (h*16+r) .. +7, word 2 gq + h of the unit for its groups gq = 0..7.
+ *
+ *   packed        [E, rows, K*bits/32] int32, the packed format   4-byte aligned
+ *   prepared_out  [E, rows, K*bits/32] int32, written; must not
+ *                 overlap `packed` (EINVAL)                      16-byte aligned
+ *
+ * rows % 16 == 0 and K % (512 / bits) == 0 (else EUNSUPPORTED); K a multiple
+ * of the group.  E * rows = 0 returns OK with no launch.  For a layer: w13 is
+ * prepared with rows = 2I, K = H; w2 with rows = H, K = I.
+ */
+int moe_wna16_prepare(const int32_t *packed, int E, int rows, int K, moe_wna16_qparams q,
+                      int32_t *prepared_out, hipStream_t stream);
+
+/*
+ * moe_wna16_forward with both projections' codes in the prepared order
+ * (scales unchanged).  Only decode-shaped calls (moe_wna16_plan reports
+ * w13_variant = w2_variant = 2: T * topk <= 4E and K in whole load units):
+ * other shapes return EUNSUPPORTED before any launch, and need the packed
+ * codes.  `events` is NULL, or 8 events recorded as by
+ * moe_wna16_forward_profiled.  Otherwise the same checks, status codes and
+ * result as moe_wna16_forward.
+ */
+int moe_wna16_forward_prepared(const void *x, const int32_t *topk_ids, const float *topk_w,
+                               const int32_t *w13_prepared, const uint16_t *w13_scales,
+                               const int32_t *w2_prepared, const uint16_t *w2_scales, int T, int H,
+                               int I, int E, int topk, moe_wna16_qparams q13,
+                               moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t *events);
+
 /* Static description of a status code (never NULL). */
 const char *moe_wna16_status_string(int status);
 

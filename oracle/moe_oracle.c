@@ -440,3 +440,52 @@ int oracle_quantize(const uint16_t *w, const float *imp, int rows, int K, int bi
     free(qbest);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Prepared code order: a one-time reorder of one projection's packed codes
+ * (model card "hampsonw/DeepSeek-V4-Flash-0731-WNA16", "What changed": signed
+ * codes packed into INT32 words, R1-R3) into blocks that the decode-shaped
+ * GPU kernels read with one 16-byte load per lane.  The pages describe no
+ * such layout; it is this library's, stated in include/moe_wna16.h, and is a
+ * pure permutation of words.  Written here from that statement in terms of K
+ * offsets: a load unit is 512/bits K elements of a row, a block 16 rows x one
+ * unit, blocks ordered [expert][row/16][unit]; slot (g*16 + r) of a block
+ * lists, group by group, the words of row r holding the codes at in-group K
+ * offsets [g*group/4, (g+1)*group/4).  2-bit codes with group 32: lane groups
+ * 2h and 2h+1 share slot (h*16 + r), which lists for groups 0..7 the word
+ * holding in-group offsets [16h, 16h+16).
+ * ------------------------------------------------------------------------- */
+int oracle_prepare(const uint32_t *packed, int E, int rows, int K, int bits, int group,
+                   uint32_t *out)
+{
+    if (E < 0 || rows < 0 || rows % 16 || K <= 0 || (bits != 2 && bits != 4) || group <= 0 ||
+        K % group || K % (512 / bits) || group % 32 || group > 512 / bits)
+        return -1;
+    const int unit = 512 / bits, nunits = K / unit, kw = K * bits / 32;
+    const int per_word = 32 / bits;                 /* codes per word */
+    const int gpu = unit / group;                   /* groups per unit */
+    for (int e = 0; e < E; ++e)
+        for (int rb = 0; rb < rows / 16; ++rb)
+            for (int u = 0; u < nunits; ++u) {
+                uint32_t *blk = out + (((size_t)e * (rows / 16) + rb) * nunits + u) * 256;
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t *row = packed + ((size_t)e * rows + rb * 16 + r) * kw;
+                    if (bits == 2 && group == 32) {
+                        for (int h = 0; h < 2; ++h)
+                            for (int gq = 0; gq < 8; ++gq) {
+                                const int k = u * unit + gq * 32 + 16 * h;
+                                blk[(h * 16 + r) * 8 + gq] = row[k / per_word];
+                            }
+                        continue;
+                    }
+                    for (int g = 0; g < 4; ++g) {
+                        int t = 0;
+                        for (int gq = 0; gq < gpu; ++gq)
+                            for (int k = g * group / 4; k < (g + 1) * group / 4; k += per_word)
+                                blk[(g * 16 + r) * 4 + t++] =
+                                    row[(u * unit + gq * group + k) / per_word];
+                    }
+                }
+            }
+    return 0;
+}

@@ -65,6 +65,8 @@ def _load():
         lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
         lib.oracle_quantize.argtypes = [P, P, i, i, i, i, i, P, P, P, P]
         lib.oracle_quantize.restype = i
+        lib.oracle_prepare.argtypes = [P, i, i, i, i, i, P]
+        lib.oracle_prepare.restype = i
         _lib = lib
     return _lib
 
@@ -209,3 +211,15 @@ def quantize(w_bf16, bits: int, group: int, ncand: int = 1, imp=None):
     if rc != 0:
         raise ValueError("oracle_quantize rejected its arguments")
     return dict(codes=codes, scales=scales, choice=choice, sums=sums)
+
+
+def prepare(packed, bits: int, group: int):
+    """Prepared block order of codes [E, rows, K*bits/32] (uint32 or int32
+    words), as oracle_prepare; returns uint32 of the same shape."""
+    w = _c(np.asarray(packed).view(np.uint32), np.uint32)
+    E, rows, kw = w.shape
+    out = np.zeros_like(w)
+    rc = _load().oracle_prepare(_ptr(w), E, rows, kw * 32 // bits, bits, group, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prepare rejected its arguments")
+    return out

@@ -38,17 +38,23 @@ def to_device(L, dev):
     )
 
 
-def run_layer(L, dev, d=None, out=None, workspace=None):
+def run_layer(L, dev, d=None, out=None, workspace=None, prepared=False):
     """Run the layer; returns (BF16 output tensor, FP32 sum as float64 numpy).
-    Also checks that the output is the RNE rounding of the FP32 sum."""
+    Also checks that the output is the RNE rounding of the FP32 sum.  With
+    prepared=True the codes are first put in the prepared order on the GPU
+    and the prepared entry point runs."""
     sp = L.spec
     d = d or to_device(L, dev)
     clamp = None if math.isinf(sp.clamp) else sp.clamp
     if workspace is None:
         workspace = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
-    y = M.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["s13"], d["w2"], d["s2"],
+    w13, w2 = d["w13"], d["w2"]
+    if prepared:
+        w13 = M.prepare(w13, sp.bits13, sp.group13)
+        w2 = M.prepare(w2, sp.bits2, sp.group2)
+    y = M.forward(d["x"], d["topk_ids"], d["topk_w"], w13, d["s13"], w2, d["s2"],
                   bits=(sp.bits13, sp.bits2), group=(sp.group13, sp.group2), alpha=sp.alpha,
-                  beta=sp.beta, clamp=clamp, out=out, workspace=workspace)
+                  beta=sp.beta, clamp=clamp, out=out, workspace=workspace, prepared=prepared)
     torch.cuda.synchronize(dev)
     if sp.T == 0:
         return y, np.zeros((0, sp.H))

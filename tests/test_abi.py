@@ -166,3 +166,46 @@ def test_quantize_rejects(lib):
     assert call(scales_out=257) == Bd.EALIGN
     # an empty matrix needs no weight, code or scale buffer
     assert call(rows=0, w=0, codes_out=0, scales_out=0) in (Bd.EHIP, Bd.EARCH, Bd.OK)
+
+
+def test_plan_sends_partial_load_units_to_tile_kernel(lib):
+    """The decode-shaped kernels walk K in units of 512/bits elements: a 2-bit
+    projection whose K is an odd multiple of 128 gets the 64-row tile kernel."""
+    ok = M.moe_wna16_plan(4, 512, 256, 8, 2, (2, 128), (2, 128))
+    assert ok["w13_variant"] == 2 and ok["block_m"] == 4
+    for H, I, q13, q2 in [(384, 256, (2, 128), (2, 128)), (512, 384, (4, 128), (2, 128)),
+                          (640, 256, (2, 64), (4, 64))]:
+        p = M.moe_wna16_plan(4, H, I, 8, 2, q13, q2)
+        assert p["w13_variant"] == 1 and p["w2_variant"] == 1 and p["block_m"] == 64, (H, I)
+    # 4-bit codes: units of 128 elements, so K = 384 stays decode-shaped
+    p = M.moe_wna16_plan(4, 384, 384, 8, 2, (4, 128), (4, 128))
+    assert p["w13_variant"] == 2
+
+
+def test_prepare_rejects(lib):
+    f = M.moe_wna16_prepare
+    assert f(256, -1, 16, 256, (4, 128), 4096, None) == Bd.EINVAL
+    assert f(256, 2, 16, 0, (4, 128), 4096, None) == Bd.EINVAL
+    assert f(256, 2, 24, 256, (4, 128), 4096, None) == Bd.EUNSUPPORTED    # rows % 16
+    assert f(256, 2, 16, 384, (2, 128), 4096, None) == Bd.EUNSUPPORTED    # 2-bit unit 256
+    assert f(256, 2, 16, 256, (3, 128), 4096, None) == Bd.EUNSUPPORTED
+    assert f(0, 2, 16, 256, (4, 128), 1 << 20, None) == Bd.EINVAL
+    assert f(256, 2, 16, 256, (4, 128), 0, None) == Bd.EINVAL
+    assert f(4096, 2, 16, 256, (4, 128), 4096 + 1024, None) == Bd.EINVAL  # overlap
+    assert f(258, 2, 16, 256, (4, 128), 1 << 20, None) == Bd.EALIGN
+    assert f(256, 2, 16, 256, (4, 128), (1 << 20) + 4, None) == Bd.EALIGN
+    assert f(0, 0, 16, 256, (4, 128), 0, None) == Bd.OK                   # nothing to do
+
+
+def test_forward_prepared_checks_like_forward(lib):
+    """Host checks run before the layout restriction: bad sizes are EINVAL."""
+    f = M.moe_wna16_forward_prepared
+    args = [16] * 7 + [4, 256, 128, 8, 2, (4, 128), (4, 128), 1.0, 0.0, float("inf"), 16, 4096,
+                        1 << 30, None]
+    bad = list(args)
+    bad[7] = -1
+    assert f(*bad) == Bd.EINVAL
+    assert f(*([0] * 7 + args[7:])) == Bd.EINVAL
+    zero = list(args)
+    zero[7] = 0
+    assert f(*zero) == Bd.OK

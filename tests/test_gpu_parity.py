@@ -126,6 +126,9 @@ SMALL = {
     "dec_w2g128_long_k": (spec(T=4, H=2048, I=1024, E=8, topk=3, bits13=2, bits2=2,
                                scale_lo=0.01, scale_hi=0.05), None, DEC),
     "dec_3_4_5_rows": (spec(T=12, H=256, I=128, E=8, topk=2), "345", DEC),
+    # 2-bit codes with K an odd multiple of 128: the tile kernel takes these
+    # small batches (the decode kernels need K in units of 256)
+    "small_batch_w2_k384": (spec(T=4, H=384, I=640, E=8, topk=2, bits13=2, bits2=2), None, PRE),
     "dec_single_expert": (spec(T=4, E=1, topk=1), None, DEC),
     # prefill-shaped
     "pre_w2_g128_g64_kc512": (spec(T=16, H=512, I=256, topk=4, bits13=2, bits2=2, group2=64,

@@ -1,0 +1,100 @@
+"""GPU parity of the prepared code order: moe_wna16_prepare against the
+oracle's statement of the layout (bit for bit), and the layer through
+moe_wna16_forward_prepared against the oracle (the same bound as the layer's
+other parity tests), at small sizes and on sampled tokens of the full
+decode-shaped workloads."""
+import numpy as np
+import pytest
+import torch
+
+import weight_only_bit_moe_amd as M
+from oracle import oracle as O
+from tests import _gpu as G
+from weight_only_bit_moe_amd import binding as Bd
+from weight_only_bit_moe_amd.inputs import LayerSpec, make_config, make_layer
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(2, 32), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128)]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return G.device()
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_prepare_matches_oracle(dev, bits, group):
+    """3 experts x 48 rows x 1024 columns: several blocks and units each."""
+    rng = np.random.default_rng(bits * 1000 + group)
+    E, rows, K = 3, 48, 1024
+    w = rng.integers(0, 2 ** 32, size=(E, rows, K * bits // 32), dtype=np.uint32)
+    got = M.prepare(torch.from_numpy(w.view(np.int32)).to(dev), bits, group)
+    torch.cuda.synchronize(dev)
+    ref = O.prepare(w, bits, group)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref)
+
+
+def spec(**kw):
+    base = dict(name="case", T=8, H=256, I=256, E=8, topk=2, bits13=4, group13=128, bits2=4,
+                group2=128, scale_lo=0.005, scale_hi=0.02)
+    base.update(kw)
+    return LayerSpec(**base)
+
+
+ACT = dict(alpha=1.702, beta=1.0, clamp=7.0)
+CASES = {
+    # one shared launch (same format on both projections)
+    "w2g128_one_launch": spec(T=4, H=1024, I=512, E=8, topk=3, bits13=2, bits2=2),
+    "w4g64_one_launch": spec(T=6, H=512, I=1024, E=16, topk=2, group13=64, group2=64, **ACT),
+    "w4g32_one_launch": spec(T=5, H=512, I=256, E=6, topk=2, group13=32, group2=32),
+    "w2g64_one_launch": spec(T=3, H=1024, I=512, E=4, topk=2, bits13=2, bits2=2, group13=64,
+                             group2=64),
+    # separate launches (formats differ, or 2-bit group 32)
+    "w4g128_w2g64": spec(T=8, H=512, I=512, E=16, topk=4, bits2=2, group2=64, **ACT),
+    "w2g32_w4g32": spec(T=6, H=512, I=256, E=8, topk=2, bits13=2, group13=32, group2=32),
+    "w2g32_both": spec(T=4, H=256, I=512, E=8, topk=2, bits13=2, group13=32, bits2=2,
+                       group2=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_forward_prepared_matches_oracle(dev, name):
+    sp = CASES[name]
+    L = make_layer(sp, seed=sum(map(ord, name)))
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                            (sp.bits2, sp.group2))
+    assert plan["w13_variant"] == 2 and plan["w2_variant"] == 2
+    _, got = G.run_layer(L, dev, prepared=True)
+    ref = O.forward_layer(L)
+    G.assert_parity(got, ref, name)
+    # the same kernels on the checkpoint order agree within the same bound
+    _, plain = G.run_layer(L, dev)
+    G.assert_parity(plain, ref, name + " (packed)")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_forward_prepared_full_workload_sampled_tokens(dev, cfg):
+    L = make_config(cfg)
+    print(f"prepared config {cfg} {L.spec.name}", flush=True)
+    _, y = G.run_layer(L, dev, prepared=True)
+    assert np.all(np.isfinite(y))
+    rows = [0, 1, L.spec.T - 1] if L.spec.T > 3 else list(range(L.spec.T))
+    G.assert_parity(y[rows], O.forward_layer(L, tokens=rows), f"config {cfg} prepared")
+
+
+def test_forward_prepared_rejects_prefill_shapes(dev):
+    """64-row tiles read the checkpoint order only: EUNSUPPORTED, nothing launched."""
+    sp = spec(T=64, H=256, I=256, E=4, topk=2)
+    L = make_layer(sp, seed=3)
+    d = G.to_device(L, dev)
+    out = torch.full((sp.T, sp.H), 7.0, dtype=torch.bfloat16, device=dev)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    st = M.moe_wna16_forward_prepared(
+        d["x"].data_ptr(), d["topk_ids"].data_ptr(), d["topk_w"].data_ptr(), d["w13"].data_ptr(),
+        d["s13"].data_ptr(), d["w2"].data_ptr(), d["s2"].data_ptr(), sp.T, sp.H, sp.I, sp.E,
+        sp.topk, (4, 128), (4, 128), 1.0, 0.0, float("inf"), out.data_ptr(), ws.data_ptr(),
+        ws.numel(), None)
+    torch.cuda.synchronize(dev)
+    assert st == Bd.EUNSUPPORTED
+    assert torch.all(out == 7.0)

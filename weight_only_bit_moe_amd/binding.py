@@ -20,7 +20,8 @@ OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP = 0, -1, -2, -3, -4, -
 #: every symbol include/moe_wna16.h declares
 EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset", "moe_wna16_plan",
             "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_align",
-            "moe_wna16_quantize", "moe_wna16_status_string")
+            "moe_wna16_quantize", "moe_wna16_prepare", "moe_wna16_forward_prepared",
+            "moe_wna16_status_string")
 
 
 class QParams(ctypes.Structure):
@@ -69,6 +70,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_wna16_align.restype = i
     lib.moe_wna16_quantize.argtypes = [P, P, i, i, QParams, i, P, P, P, P]
     lib.moe_wna16_quantize.restype = i
+    lib.moe_wna16_prepare.argtypes = [P, i, i, i, QParams, P, P]
+    lib.moe_wna16_prepare.restype = i
+    lib.moe_wna16_forward_prepared.argtypes = lib.moe_wna16_forward.argtypes + [P]
+    lib.moe_wna16_forward_prepared.restype = i
     lib.moe_wna16_status_string.argtypes = [i]
     lib.moe_wna16_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -134,6 +139,21 @@ def moe_wna16_forward_profiled(x, topk_ids, topk_w, w13_packed, w13_scales, w2_p
         events)
 
 
+def moe_wna16_forward_prepared(x, topk_ids, topk_w, w13_prepared, w13_scales, w2_prepared,
+                               w2_scales, T, H, I, E, topk, q13, q2, alpha, beta, clamp, out,
+                               workspace, workspace_bytes, stream, events=None) -> int:
+    """Raw entry point; codes in the prepared order; `events` None or 8 hipEvent_t."""
+    return load_library().moe_wna16_forward_prepared(
+        x, topk_ids, topk_w, w13_prepared, w13_scales, w2_prepared, w2_scales, T, H, I, E, topk,
+        QParams(*q13), QParams(*q2), alpha, beta, clamp, out, workspace, workspace_bytes, stream,
+        events)
+
+
+def moe_wna16_prepare(packed, E, rows, K, q, prepared_out, stream) -> int:
+    """Raw entry point on integer device addresses; returns the status."""
+    return load_library().moe_wna16_prepare(packed, E, rows, K, QParams(*q), prepared_out, stream)
+
+
 def moe_wna16_align(topk_ids, T, topk, E, block_m, sorted_ids, tile_expert, expert_offsets,
                     inv_perm, num_tiles, bad_ids, stream) -> int:
     """Raw entry point on integer device addresses; returns the status."""
@@ -179,13 +199,15 @@ def workspace_for(T, H, I, E, topk, device):
 
 def forward(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, *,
             bits=(4, 4), group=(128, 128), alpha: float = 1.0, beta: float = 0.0,
-            clamp: Optional[float] = None, out=None, workspace=None):
+            clamp: Optional[float] = None, out=None, workspace=None, prepared: bool = False):
     """Routed WNA16 MoE layer on torch tensors (see include/moe_wna16.h).
 
     x [T, H] bf16; topk_ids [T, k] int32; topk_w [T, k] float32;
     w13_packed [E, 2I, H*b13/32] int32 (or uint32 bits); w13_scales [E, 2I, H/g13] fp16;
     w2_packed [E, H, I*b2/32] int32; w2_scales [E, H, I/g2] fp16.
-    `bits` and `group` are (w13, w2) pairs.  Returns out [T, H] bf16.
+    `bits` and `group` are (w13, w2) pairs.  With prepared=True the two code
+    tensors hold the output of prepare() (same shapes) and the call must be
+    decode-shaped.  Returns out [T, H] bf16.
     """
     torch = _torch()
     dev = x.device
@@ -219,13 +241,34 @@ def forward(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, *
         workspace = workspace_for(T, H, I, E, topk, dev)
     _check(workspace, "workspace", (torch.uint8,), dev)
     c = math.inf if clamp is None else float(clamp)
-    st = moe_wna16_forward(
-        x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w13_packed.data_ptr(),
-        w13_scales.data_ptr(), w2_packed.data_ptr(), w2_scales.data_ptr(), T, H, I, E, topk,
-        (b13, g13), (b2, g2), float(alpha), float(beta), c, out.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), _stream(dev))
+    args = (x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w13_packed.data_ptr(),
+            w13_scales.data_ptr(), w2_packed.data_ptr(), w2_scales.data_ptr(), T, H, I, E, topk,
+            (b13, g13), (b2, g2), float(alpha), float(beta), c, out.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), _stream(dev))
+    if prepared:
+        st, name = moe_wna16_forward_prepared(*args), "moe_wna16_forward_prepared"
+    else:
+        st, name = moe_wna16_forward(*args), "moe_wna16_forward"
     if st != OK:
-        raise MoeWna16Error(st, "moe_wna16_forward")
+        raise MoeWna16Error(st, name)
+    return out
+
+
+def prepare(packed, bits: int, group: int):
+    """Prepared block order of one projection's codes [E, rows, K*bits/32]
+    (int32 or uint32, on the GPU): a new int32 tensor of the same shape."""
+    torch = _torch()
+    dev = packed.device
+    _check(packed, "packed", (torch.int32, torch.uint32), dev)
+    if packed.dim() != 3:
+        raise ValueError("packed must be [E, rows, K*bits/32]")
+    E, rows, kw = packed.shape
+    K = kw * 32 // bits
+    out = torch.empty((E, rows, kw), dtype=torch.int32, device=dev)
+    st = moe_wna16_prepare(packed.data_ptr(), E, rows, K, (bits, group), out.data_ptr(),
+                           _stream(dev))
+    if st != OK:
+        raise MoeWna16Error(st, "moe_wna16_prepare")
     return out
 
 

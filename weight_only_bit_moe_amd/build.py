@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_wna16.so")
-SOURCES = ["kernels.hip", "quantize.hip", "api.hip"]
+SOURCES = ["kernels.hip", "quantize.hip", "prepare.hip", "api.hip"]
 ARCH = "gfx950"
 
 

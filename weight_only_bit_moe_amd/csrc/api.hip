@@ -92,8 +92,11 @@ void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
                moe_wna16_qparams q2, moe_wna16_plan_t *plan)
 {
     const long long P = (long long)T * topk;
+    // the decode-shaped kernels walk K in whole load units of 512 / bits
+    // elements (256 for 2-bit, 128 for 4-bit codes)
     const bool decode = P <= 4LL * E && wna16::decode_lds_bytes(H, q13.group) <= 65536 &&
-                        wna16::decode_lds_bytes(I, q2.group) <= 65536;
+                        wna16::decode_lds_bytes(I, q2.group) <= 65536 &&
+                        H % (512 / q13.bits) == 0 && I % (512 / q2.bits) == 0;
     const int bm = decode ? wna16::kDecodeRows : 64;
     plan->block_m = bm;
     plan->max_tiles = (int)(P / bm + (E < P ? E : P));
@@ -200,7 +203,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
                       int E, int topk, moe_wna16_qparams q13, moe_wna16_qparams q2, float alpha,
                       float beta, float clamp, void *out, void *workspace,
                       size_t workspace_bytes, hipStream_t stream,
-                        const hipEvent_t *events)
+                      const hipEvent_t *events, bool prepared)
 {
     int st = check_sizes(T, H, I, E, topk);
     if (st != MOE_WNA16_OK)
@@ -229,6 +232,8 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
 
     moe_wna16_plan_t plan;
     make_plan(T, H, I, E, topk, q13, q2, &plan);
+    if (prepared && (plan.w13_variant != 2 || plan.w2_variant != 2))
+        return MOE_WNA16_EUNSUPPORTED;   // prepared codes feed the decode-shaped kernels only
     LayerDims d{};
     d.T = T;
     d.H = H;
@@ -246,6 +251,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     d.alpha = alpha;
     d.beta = beta;
     d.clamp = clamp;
+    d.prepared = prepared ? 1 : 0;
 
     char *base = static_cast<char *>(workspace);
     Workspace ws{};
@@ -307,7 +313,7 @@ int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_
 {
     return forward_impl(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
                         I, E, topk, q13, q2, alpha, beta, clamp, out, workspace, workspace_bytes,
-                        stream, nullptr);
+                        stream, nullptr, false);
 }
 
 int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const float *topk_w,
@@ -322,7 +328,46 @@ int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const flo
         return MOE_WNA16_EINVAL;
     return forward_impl(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
                         I, E, topk, q13, q2, alpha, beta, clamp, out, workspace, workspace_bytes,
-                        stream, events);
+                        stream, events, false);
+}
+
+int moe_wna16_forward_prepared(const void *x, const int32_t *topk_ids, const float *topk_w,
+                               const int32_t *w13_prepared, const uint16_t *w13_scales,
+                               const int32_t *w2_prepared, const uint16_t *w2_scales, int T, int H,
+                               int I, int E, int topk, moe_wna16_qparams q13,
+                               moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t *events)
+{
+    return forward_impl(x, topk_ids, topk_w, w13_prepared, w13_scales, w2_prepared, w2_scales, T,
+                        H, I, E, topk, q13, q2, alpha, beta, clamp, out, workspace,
+                        workspace_bytes, stream, events, true);
+}
+
+int moe_wna16_prepare(const int32_t *packed, int E, int rows, int K, moe_wna16_qparams q,
+                      int32_t *prepared_out, hipStream_t stream)
+{
+    if (E < 0 || rows < 0 || K <= 0)
+        return MOE_WNA16_EINVAL;
+    if (!valid_qparams(q) || K % q.group || K % (512 / q.bits) || rows % 16)
+        return MOE_WNA16_EUNSUPPORTED;
+    const size_t bytes = (size_t)E * rows * (K / 32 * q.bits) * 4;
+    if (bytes == 0)
+        return MOE_WNA16_OK;
+    if (!packed || !prepared_out)
+        return MOE_WNA16_EINVAL;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(packed),
+                    b = reinterpret_cast<uintptr_t>(prepared_out);
+    if (a < b + bytes && b < a + bytes)
+        return MOE_WNA16_EINVAL;   // the reorder cannot run in place
+    if (!aligned(packed, 4) || !aligned(prepared_out, 16))
+        return MOE_WNA16_EALIGN;
+    const int st = check_device();
+    if (st != MOE_WNA16_OK)
+        return st;
+    return hip_status(wna16::launch_prepare(reinterpret_cast<const uint32_t *>(packed), E, rows,
+                                            K, q.bits, q.group,
+                                            reinterpret_cast<uint32_t *>(prepared_out), stream));
 }
 
 int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
 struct GemmArgs {
     const uint16_t *a;        // W13: x_perm [T][K]; W2: act [slots][K]
     const float *a_bias;      // negated bias terms; W13: x_bias [T][K/gs]; W2: act_bias [slots][K/gs]
-    const uint32_t *codes;    // [E][rows][K*bits/32]
+    const uint32_t *codes;    // [E][rows][K*bits/32], or the prepared block order (prepared = 1)
     const uint16_t *scales;   // [E][rows][K/gs]
     const int32_t *sorted_ids;
     const int32_t *tile_expert;
@@ -376,6 +376,7 @@ struct GemmArgs {
     int P, topk;
     int bits_next, gs_next;   // W13 epilogue: format of the w2 operand
     float alpha, beta, clamp;
+    int prepared;             // codes in the prepared block order (decode-shaped kernels only)
 };
 
 template <int BITS, int GS>
@@ -1088,7 +1089,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // holds, for each group of the unit, the dwords its MFMA fragments need
 // (dwords [g*n, g*n + n) of the group with n = gs*bits/128).
 // ---------------------------------------------------------------------------
-template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false>
+template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false, bool PREP = false>
 struct Stream {
     static constexpr int R = 4;                      // rows per tile
     static constexpr int NW = 4;                     // waves per workgroup
@@ -1111,6 +1112,23 @@ struct Stream {
     static __device__ __forceinline__ void load_unit(uint32_t (&dst)[NB][UDW],
                                                      const uint32_t *const *brow, int u, int g)
     {
+        if constexpr (PREP) {
+            // prepared blocks: this lane's words of unit u sit together, in
+            // register order (brow already points at the lane's slot)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint32_t *p = brow[j] + (size_t)u * kPrepBlockDwords;
+#pragma unroll
+                for (int h = 0; h < UDW / 4; ++h) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p + 4 * h);
+                    dst[j][4 * h + 0] = v[0];
+                    dst[j][4 * h + 1] = v[1];
+                    dst[j][4 * h + 2] = v[2];
+                    dst[j][4 * h + 3] = v[3];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const uint32_t *p = brow[j] + u * 16;
@@ -1136,7 +1154,9 @@ struct Stream {
     // Regroup the loaded dwords across lane groups (see above).
     static __device__ __forceinline__ void regroup(uint32_t (&r)[UDW])
     {
-        if constexpr (!SPLIT && GPU == 2) {
+        if constexpr (PREP) {
+            // prepared blocks already hold the registers in this order
+        } else if constexpr (!SPLIT && GPU == 2) {
             const auto a = __builtin_amdgcn_permlane16_swap(r[0], r[2], false, false);
             const auto b = __builtin_amdgcn_permlane16_swap(r[1], r[3], false, false);
             r[0] = a[0];
@@ -1306,6 +1326,7 @@ struct Stream {
         // this lane's weight rows
         const int nrows = W13 ? 2 * args.N : args.N;
         const int kw = K * BITS / 32;
+        const int nunits = K / UK;   // K % UK == 0: the plan sends other K to tile_kernel
         const uint32_t *brow[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -1314,9 +1335,12 @@ struct Stream {
                 n = nb * BN + wave * COLS + (j % (NB / 2)) * 16 + c + (j >= NB / 2 ? args.N : 0);
             else
                 n = nb * BN + wave * COLS + j * 16 + c;
-            brow[j] = args.codes + ((size_t)e * nrows + n) * kw;
+            if constexpr (PREP)   // block (row / 16, unit 0), this lane's slot
+                brow[j] = args.codes + ((size_t)e * (nrows / 16) + n / 16) * nunits * kPrepBlockDwords +
+                          prep_block_dword(BITS, GS, g, c, 0);
+            else
+                brow[j] = args.codes + ((size_t)e * nrows + n) * kw;
         }
-        const int nunits = K / UK;
 
         // The weight stream starts first: its HBM latency overlaps the staging.
         uint32_t q[D][NB][UDW];
@@ -1573,11 +1597,11 @@ struct Stream {
     }
 };
 
-template <int BITS, int GS, int NB, int D, bool W13>
+template <int BITS, int GS, int NB, int D, bool W13, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void stream_kernel(
     const GemmArgs args)
 {
-    Stream<BITS, GS, NB, D, W13>::run(args, blockIdx.x, blockIdx.y);
+    Stream<BITS, GS, NB, D, W13, false, PREP>::run(args, blockIdx.x, blockIdx.y);
 }
 
 // Both decode-shaped GEMMs in one launch: workgroups [0, n13) are the w13
@@ -1585,15 +1609,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 // are dispatched in id order, so every w13 item has been dispatched before
 // any w2 item waits for its tile's w13 items; a w2 item streams its first
 // weights while it waits.
-template <int B13, int G13, int D13, int B2, int G2, int D2>
+template <int B13, int G13, int D13, int B2, int G2, int D2, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_kernel(
     const GemmArgs a13, const GemmArgs a2, int max_tiles, int nblk13, int nblk2)
 {
     const int id = blockIdx.x, n13 = max_tiles * nblk13;
     if (id < n13)
-        Stream<B13, G13, 2, D13, true, true>::run(a13, id / nblk13, id % nblk13);
+        Stream<B13, G13, 2, D13, true, true, PREP>::run(a13, id / nblk13, id % nblk13);
     else
-        Stream<B2, G2, 2, D2, false, true>::run(a2, (id - n13) / nblk2, (id - n13) % nblk2);
+        Stream<B2, G2, 2, D2, false, true, PREP>::run(a2, (id - n13) / nblk2,
+                                                      (id - n13) % nblk2);
 }
 
 __global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restrict__ dst,
@@ -1675,6 +1700,21 @@ static constexpr int stream_depth()
     return S1::SPLIT ? 1 : S1::GPU == 4 ? 2 : (BITS == 4 && GS == 128) ? 8 : 4;
 }
 
+template <int BITS, int GS, int NB, int D, bool W13>
+static void launch_stream(const GemmArgs &a, dim3 grid, hipStream_t stream,
+                          const KernelEvents &ev)
+{
+    using K_ = Stream<BITS, GS, NB, D, W13>;
+    if (a.prepared)
+        hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, D, W13, true>), grid,
+                              dim3(K_::NTHREADS), (uint32_t)K_::lds_bytes(a.K), stream, ev.start,
+                              ev.stop, 0, a);
+    else
+        hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, D, W13, false>), grid,
+                              dim3(K_::NTHREADS), (uint32_t)K_::lds_bytes(a.K), stream, ev.start,
+                              ev.stop, 0, a);
+}
+
 // Tile shapes.  Variant 2 (few rows per expert, HBM-bound): the stream kernel
 // on 4-row tiles.  Variant 1 (many rows per expert, MFMA-bound): the tile
 // kernel on 64-row tiles.
@@ -1686,17 +1726,14 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
         constexpr int NB = 2;
         constexpr int D = stream_depth<BITS, GS, W13>();
         using K_ = Stream<BITS, GS, NB, D, W13>;
-        using K1 = Stream<BITS, GS, NB, 1, W13>;
         const dim3 grid(max_tiles, a.N / K_::BN);
         if ((a.K / K_::UK) % D == 0)
-            hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, D, W13>), grid,
-                                  dim3(K_::NTHREADS), (uint32_t)K_::lds_bytes(a.K), stream,
-                                  ev.start, ev.stop, 0, a);
+            launch_stream<BITS, GS, NB, D, W13>(a, grid, stream, ev);
         else
-            hipExtLaunchKernelGGL((stream_kernel<BITS, GS, NB, 1, W13>), grid,
-                                  dim3(K1::NTHREADS), (uint32_t)K1::lds_bytes(a.K), stream,
-                                  ev.start, ev.stop, 0, a);
+            launch_stream<BITS, GS, NB, 1, W13>(a, grid, stream, ev);
     } else {
+        if (a.prepared)   // the tile kernel reads the checkpoint layout only
+            return hipErrorNotSupported;
         using K_ = Tile<BITS, GS, W13>;
         const long items = (long)max_tiles * ((a.N + K_::OUTC - 1) / K_::OUTC);
         const long grid = (items + K_::kXcds - 1) / K_::kXcds * K_::kXcds;
@@ -1744,6 +1781,7 @@ static GemmArgs w13_args(const int32_t *w13, const uint16_t *s13, const LayerDim
     a.beta = d.beta;
     a.clamp = d.clamp;
     a.tile_done = ws.tile_done;
+    a.prepared = d.prepared;
     return a;
 }
 
@@ -1774,6 +1812,7 @@ static GemmArgs w2_args(const int32_t *w2, const uint16_t *s2, const float *topk
     a.P = d.T * d.topk;
     a.topk = d.topk;
     a.tile_done = ws.tile_done;
+    a.prepared = d.prepared;
     return a;
 }
 
@@ -1795,10 +1834,16 @@ static hipError_t decode_dispatch(const GemmArgs &a13, GemmArgs a2, int max_tile
     const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
     a2.tile_target = nblk13;
     const size_t l13 = S13::lds_bytes(a13.K), l2 = S2::lds_bytes(a2.K);
-    hipExtLaunchKernelGGL((decode_kernel<BITS, GS, D13, BITS, GS, D2>),
-                          dim3((unsigned)(max_tiles * (nblk13 + nblk2))), dim3(S13::NTHREADS),
-                          (uint32_t)(l13 > l2 ? l13 : l2), stream, ev.start, ev.stop, 0, a13,
-                          a2, max_tiles, nblk13, nblk2);
+    const dim3 grid((unsigned)(max_tiles * (nblk13 + nblk2)));
+    const uint32_t lds = (uint32_t)(l13 > l2 ? l13 : l2);
+    if (a13.prepared)
+        hipExtLaunchKernelGGL((decode_kernel<BITS, GS, D13, BITS, GS, D2, true>), grid,
+                              dim3(S13::NTHREADS), lds, stream, ev.start, ev.stop, 0, a13, a2,
+                              max_tiles, nblk13, nblk2);
+    else
+        hipExtLaunchKernelGGL((decode_kernel<BITS, GS, D13, BITS, GS, D2, false>), grid,
+                              dim3(S13::NTHREADS), lds, stream, ev.start, ev.stop, 0, a13, a2,
+                              max_tiles, nblk13, nblk2);
     return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct LayerDims {
     int bits13, g13, bits2, g2;
     int block_m, max_tiles, variant13, variant2;
     float alpha, beta, clamp;
+    int prepared;   // codes in the prepared block order (decode-shaped plans only)
 };
 
 // Expert-sorted tiles + activation reorder/bias + zeroed accumulator.
@@ -67,6 +68,10 @@ bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I);
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
+// Prepared block order of one projection's codes (prepare.hip): packed
+// [E][rows][K*bits/32] -> blocks [E][rows/16][K/(512/bits)] of 256 words.
+hipError_t launch_prepare(const uint32_t *packed, int E, int rows, int K, int bits, int group,
+                          uint32_t *prepared, hipStream_t stream);
 // Quantizer (quantize.hip): W [rows][K] BF16 -> codes, FP16 scales and the
 // four reconstruction error sums.
 hipError_t launch_quantize(const uint16_t *w, const float *imp, int rows, int K, int bits,

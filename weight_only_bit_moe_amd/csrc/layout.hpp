@@ -83,4 +83,36 @@ WNA16_HD int frag_bias_weight(int bits, int gs, int pos)
     return 128 + ((1 << (bits - 1)) << frag_shift(bits, gs, pos));
 }
 
+// Prepared code layout (written once by moe_wna16_prepare, read by the
+// decode-shaped kernels).  A load unit is UK = 512 / bits consecutive K
+// elements of one row (16 dwords: 1, 2, 4 or 8 quantization groups).  The
+// codes of 16 rows x one unit form a block; blocks are stored
+// [expert][row / 16][unit].  Inside a block, lane l = 16 g + c (row c of the
+// 16, lane group g) finds at dwords l * 4 .. l * 4 + 3 the code words its MFMA
+// fragments read, in register order: for each group of the unit in turn, the
+// words holding lane group g's codes of that group (in-group K offsets
+// [g * gs / 4, (g + 1) * gs / 4), see frag_src).  2-bit codes with gs = 32
+// hold only 8 codes per lane group and group, half a word; lane groups 2h and
+// 2h + 1 share word h of each group, so that block stores 32 lanes x 8 words,
+// lane h * 16 + c at dwords (h * 16 + c) * 8 .. + 7, one word per group.
+constexpr int kPrepBlockDwords = 256;
+
+// Dword of the row's unit (0..15) that register t of lane group g holds.
+WNA16_HD int prep_src_dword(int bits, int gs, int g, int t)
+{
+    if (bits == 2 && gs == 32)           // t = group (0..7), g / 2 = half
+        return 2 * t + (g >> 1);
+    const int per = gs * bits / 128;     // words per lane group and group: 4, 2 or 1
+    const int words = gs * bits / 32;    // words per group
+    return (t / per) * words + g * per + t % per;
+}
+
+// Dword offset, inside a block, of register t of lane (g, c).
+WNA16_HD int prep_block_dword(int bits, int gs, int g, int c, int t)
+{
+    if (bits == 2 && gs == 32)
+        return ((g >> 1) * 16 + c) * 8 + t;
+    return (g * 16 + c) * 4 + t;
+}
+
 }  // namespace wna16
