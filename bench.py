@@ -12,12 +12,20 @@ The default workload is the decode-sized W2A16 layer (T=4, hidden 4096,
 intermediate 2048, 256 experts, top-6, 2-bit codes, group 128), which is
 HBM-bound; `--config 3/4/5` selects the other workloads.
 
+Decode-shaped workloads run on codes in the prepared order by default: the
+one-time moe_wna16_prepare reorder runs before warmup, outside the timed
+region, and every step calls moe_wna16_forward_prepared (`--codes packed`
+times the checkpoint order through moe_wna16_forward instead).  Prefill-shaped
+workloads always use the checkpoint order.
+
 Prints ONE JSON line.  `value` and `ms_per_step` come from K steps through the
-plain entry point (moe_wna16_forward).  The same K steps are then run again
-through moe_wna16_forward_profiled, whose kernel dispatches carry their own
-start/stop events; `roofline` is for the kernel with the longest average
-duration in that pass.  `cpu_baseline` is the CPU oracle on a bounded sample
-of the same workload.
+plain entry point (no events).  The same K steps are then run again with
+per-launch events (moe_wna16_forward_profiled, or the prepared entry with its
+event array), whose kernel dispatches carry their own start/stop events;
+`roofline` is for the kernel with the longest average duration in that pass.
+`cpu_baseline` is the CPU oracle on a bounded sample of the same workload.
+
+`--quantize` measures the quantizer instead and prints its own line.
 """
 import argparse
 import ctypes
@@ -52,9 +60,11 @@ def parse():
                     help="CPU time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--traffic-file", default=None,
                     help="rocprofv3 counter summary holding the dominant kernel's HBM traffic")
-    ap.add_argument("--prepared", action="store_true",
-                    help="decode-shaped workloads: codes in the prepared order "
-                         "(moe_wna16_prepare once, then moe_wna16_forward_prepared)")
+    ap.add_argument("--codes", choices=["auto", "prepared", "packed"], default="auto",
+                    help="code order: 'prepared' (moe_wna16_prepare once, outside the timed "
+                         "region, then moe_wna16_forward_prepared; decode-shaped workloads "
+                         "only), 'packed' (the checkpoint order), 'auto' = prepared for "
+                         "decode-shaped workloads, packed otherwise")
     ap.add_argument("--quantize", action="store_true",
                     help="measure the quantizer instead of the layer (its own JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -161,6 +171,14 @@ def main():
     sp = L.spec
     T, H, I, E, k = sp.T, sp.H, sp.I, sp.E, sp.topk
     P = T * k
+    q13, q2 = (sp.bits13, sp.group13), (sp.bits2, sp.group2)
+    plan = M.moe_wna16_plan(T, H, I, E, k, q13, q2)
+    decode_shaped = plan["w13_variant"] == 2 and plan["w2_variant"] == 2
+    if args.codes == "prepared" and not decode_shaped:
+        print("--codes prepared needs a decode-shaped workload (--config 2 or 3)",
+              file=sys.stderr)
+        sys.exit(2)
+    args.prepared = args.codes == "prepared" or (args.codes == "auto" and decode_shaped)
     w13 = torch.from_numpy(L.w13.view(np.int32)).to(dev)
     s13 = torch.from_numpy(L.s13).to(dev)
     w2 = torch.from_numpy(L.w2.view(np.int32)).to(dev)
@@ -181,7 +199,6 @@ def main():
     ws = M.workspace_for(T, H, I, E, k, dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    q13, q2 = (sp.bits13, sp.group13), (sp.bits2, sp.group2)
     clamp = sp.clamp
     fixed = (w13.data_ptr(), s13.data_ptr(), w2.data_ptr(), s2.data_ptr())
     call_args = []
@@ -189,11 +206,6 @@ def main():
         call_args.append((x.data_ptr(), ids.data_ptr(), w.data_ptr()) + fixed +
                          (T, H, I, E, k, q13, q2, sp.alpha, sp.beta, clamp, out.data_ptr(),
                           ws.data_ptr(), ws.numel(), stream))
-    plan = M.moe_wna16_plan(T, H, I, E, k, q13, q2)
-    if args.prepared and (plan["w13_variant"] != 2 or plan["w2_variant"] != 2):
-        print("--prepared needs a decode-shaped workload (--config 2 or 3)", file=sys.stderr)
-        sys.exit(2)
-
     def step_plain(i):
         if args.prepared:
             st = M.moe_wna16_forward_prepared(*call_args[i % nb], None)
