@@ -98,3 +98,68 @@ def test_forward_prepared_rejects_prefill_shapes(dev):
     torch.cuda.synchronize(dev)
     assert st == Bd.EUNSUPPORTED
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("HI", [256, 1024])   # separate / shared decode launches
+def test_forward_prepared_edge_ids(dev, HI):
+    """Invalid, out-of-range and duplicate ids and an empty expert, on
+    prepared codes."""
+    sp = spec(T=10, H=HI, I=HI, topk=3, E=8)
+    L = make_layer(sp, seed=177)
+    ids = L.topk_ids.copy()
+    ids[0, 1] = -1
+    ids[1, 2] = 8
+    ids[2, 0] = 1000
+    ids[3, 1] = ids[3, 0]
+    ids[ids == 5] = 6
+    L.topk_ids = ids.astype(np.int32)
+    _, got = G.run_layer(L, dev, prepared=True)
+    G.assert_parity(got, O.forward_layer(L), "edge ids, prepared")
+
+
+@pytest.mark.parametrize("HI", [256, 1024])
+def test_forward_prepared_all_ids_invalid_writes_zeros(dev, HI):
+    sp = spec(T=4, H=HI, I=HI, topk=2, E=8)
+    L = make_layer(sp, seed=179)
+    L.topk_ids[:, :] = -1
+    out = torch.full((sp.T, sp.H), 3.0, dtype=torch.bfloat16, device=dev)
+    y, got = G.run_layer(L, dev, out=out, prepared=True)
+    assert not G.to_f64(y).any()
+    G.assert_parity(got, O.forward_layer(L), "all ids invalid, prepared")
+
+
+def test_forward_prepared_events_bracket_the_launches(dev):
+    """With an event array the prepared entry records launch start/stop
+    events in stream order (one shared w13 + w2 launch here)."""
+    import ctypes
+
+    from bench import Hip
+
+    sp = spec(T=4, H=1024, I=1024, E=8, topk=2, bits13=2, bits2=2)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (2, 128), (2, 128))
+    assert plan["gemms_one_launch"] == 1 and plan["convert_in_w2"] == 1
+    L = make_layer(sp, seed=181)
+    d = G.to_device(L, dev)
+    w13 = M.prepare(d["w13"], 2, 128)
+    w2 = M.prepare(d["w2"], 2, 128)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    out = torch.empty((sp.T, sp.H), dtype=torch.bfloat16, device=dev)
+    hip = Hip()
+    ev = (ctypes.c_void_p * 8)(*[hip.event() for _ in range(8)])
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = M.moe_wna16_forward_prepared(
+        d["x"].data_ptr(), d["topk_ids"].data_ptr(), d["topk_w"].data_ptr(), w13.data_ptr(),
+        d["s13"].data_ptr(), w2.data_ptr(), d["s2"].data_ptr(), sp.T, sp.H, sp.I, sp.E, sp.topk,
+        (2, 128), (2, 128), 1.0, 0.0, float("inf"), out.data_ptr(), ws.data_ptr(), ws.numel(),
+        stream, ev)
+    assert st == Bd.OK
+    torch.cuda.synchronize(dev)
+    assert hip.elapsed_ms(ev[0], ev[1]) >= 0.0      # route
+    assert hip.elapsed_ms(ev[2], ev[5]) >= 0.0      # the shared w13 + w2 launch
+    assert hip.elapsed_ms(ev[1], ev[2]) >= 0.0      # in stream order
+    f32 = M.workspace_f32_sum(ws, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16),
+                          G.f32_to_bf16_bits(f32))
+    G.assert_parity(f32.astype(np.float64), O.forward_layer(L), "prepared, with events")
+    for e in ev:
+        hip.destroy(e)
