@@ -35,6 +35,17 @@ def test_prepare_matches_oracle(dev, bits, group):
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ref)
 
 
+@pytest.mark.parametrize("bits,group,E,rows,K", [(4, 128, 1, 16, 128), (2, 32, 1, 16, 256),
+                                                 (2, 128, 2, 16, 256)])
+def test_prepare_single_block(dev, bits, group, E, rows, K):
+    """One block per expert (16 rows x one load unit)."""
+    rng = np.random.default_rng(E * rows + K + bits)
+    w = rng.integers(0, 2 ** 32, size=(E, rows, K * bits // 32), dtype=np.uint32)
+    got = M.prepare(torch.from_numpy(w.view(np.int32)).to(dev), bits, group)
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), O.prepare(w, bits, group))
+
+
 def spec(**kw):
     base = dict(name="case", T=8, H=256, I=256, E=8, topk=2, bits13=4, group13=128, bits2=4,
                 group2=128, scale_lo=0.005, scale_hi=0.02)

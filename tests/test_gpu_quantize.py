@@ -186,3 +186,16 @@ def test_quantize_full_workload_sampled_rows(dev, spec):
     assert sums[0] < sums[1] and sums[2] < sums[3]
     w2 = sum(float((w[i:i + 65536].double() ** 2).sum()) for i in range(0, spec.rows, 65536))
     np.testing.assert_allclose(sums[1], w2, rtol=1e-9)
+
+
+@pytest.mark.parametrize("bits,group,rows,K", [(2, 32, 1, 32), (4, 32, 3, 32), (2, 128, 2, 128),
+                                               (4, 64, 5, 192)])
+def test_quantize_smallest_shapes(dev, bits, group, rows, K):
+    """One group per row (a strip with a single active lane group), and K
+    smaller than a 1024-column strip."""
+    w = make_dense_weights(rows, K, rows * 100 + K)
+    imp = make_importance(K, 5)
+    for ncand in (1, 4):
+        got = gpu_quantize(w, bits, group, ncand, imp, dev)
+        ref = O.quantize(w, bits, group, ncand, imp)
+        assert_quant_parity(w, bits, group, ncand, imp, got, ref, max_ties=1)

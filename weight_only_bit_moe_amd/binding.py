@@ -309,7 +309,7 @@ def quantize(w, bits: int, group: int, n_candidates: int = 1, imp=None):
         if imp.shape != (K,):
             raise ValueError(f"imp must have shape ({K},)")
     codes = torch.empty((rows, K * bits // 32), dtype=torch.int32, device=dev)
-    scales = torch.empty((rows, max(K // group, 1)), dtype=torch.float16, device=dev)
+    scales = torch.empty((rows, K // group), dtype=torch.float16, device=dev)
     sums = torch.empty(4, dtype=torch.float64, device=dev)
     st = moe_wna16_quantize(w.data_ptr() if rows else None,
                             None if imp is None else imp.data_ptr(), rows, K, (bits, group),
@@ -317,4 +317,4 @@ def quantize(w, bits: int, group: int, n_candidates: int = 1, imp=None):
                             scales.data_ptr() if rows else None, sums.data_ptr(), _stream(dev))
     if st != OK:
         raise MoeWna16Error(st, "moe_wna16_quantize")
-    return dict(codes=codes, scales=scales[:, :K // group], sums=sums)
+    return dict(codes=codes, scales=scales, sums=sums)
