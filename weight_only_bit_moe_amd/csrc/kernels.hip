@@ -497,17 +497,14 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
 // (already in fragment order), codes, scales and the rows' bias terms -- is
 // copied from memory straight into LDS (global_load_lds, no registers) in
 // the order the MFMA lanes read it, so each read is one ds_read.  The copies
-// run 2-3 chunks ahead through a ring of LDS stages with explicit vmcnt
-// waits.
+// run up to STAGES - 1 chunks ahead (1 to 3) through a ring of LDS stages
+// with explicit vmcnt waits, spread in small batches over the chunk's work.
 //
-// Work per chunk and wave has two halves: a VALU half that reads the
-// chunk's codes and unpacks them to BF16 fragments, and an MFMA half that
-// runs the chains (and folds each group's chain into the FP32 accumulators
-// with its scale).  Waves 0-3 and 4-7 -- one of each on every SIMD -- run
-// the halves in alternation, half a chunk apart, so that on every SIMD one
-// wave issues MFMAs while the other keeps the VALU busy; a barrier between
-// halves keeps the two groups in step, and the MFMA half runs at a raised
-// wave priority.
+// Work per chunk and wave: read the chunk's codes and unpack them to BF16
+// fragments (VALU), then run the chains of every active row subtile and fold
+// each group's chain into the FP32 accumulators with its scale (MFMA, with
+// the fold and the next subtile's LDS reads under the MFMAs).  Both waves of
+// a SIMD do the same; one barrier per chunk keeps the ring consistent.
 //
 // Workgroup ids are spread over the 8 XCDs round-robin by the hardware; the
 // kernel gives each XCD a contiguous run of (tile, column block) items,
