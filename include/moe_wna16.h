@@ -23,7 +23,9 @@
  *     allocates no memory and keeps no state between calls; calls on
  *     different streams may run concurrently.
  *   - Work is enqueued asynchronously on `stream`; no entry point
- *     synchronises the host.
+ *     synchronises the host.  The enqueued work is kernels only (no memset
+ *     or copy nodes), so the calls can be captured into a HIP graph and
+ *     replayed; the layer keeps no state in the workspace between calls.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     non-zero status means nothing was launched and no buffer was touched.
  *   - Device-side values (expert ids) are not validated on the host: an id
