@@ -294,41 +294,39 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         return;
     }
     if (blk < nalign + nprep) {
+        // GS / 8 consecutive threads per (token, group), 8 fragment
+        // positions each (one 16-byte store); the group's bias term is
+        // summed across them with shuffles
+        constexpr int PL = GS / 8;
         const int ngroups = H / GS;
         const int gid = (blk - nalign) * kAlignThreads + threadIdx.x;
-        if (gid >= T * ngroups)
-            return;
-        const int t = gid / ngroups, G = gid % ngroups;
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + (size_t)t * H + (size_t)G * GS);
-        uint32_t w[GS / 2];
+        const bool on = gid < T * ngroups * PL;   // whole groups: PL divides the block
+        const int q = gid % PL, tg = gid / PL;
+        const int t = on ? tg / ngroups : 0, G = on ? tg % ngroups : 0;
+        const uint16_t *src = x + (size_t)t * H + (size_t)G * GS;
+        uint32_t e[8];
 #pragma unroll
-        for (int q = 0; q < GS / 8; ++q) {
-            const u32x4_t v = src[q];
-            w[4 * q + 0] = v[0];
-            w[4 * q + 1] = v[1];
-            w[4 * q + 2] = v[2];
-            w[4 * q + 3] = v[3];
-        }
+        for (int v = 0; v < 8; ++v)
+            e[v] = on ? src[frag_src(BITS, GS, q * 8 + v)] : 0u;
         float sum = 0.f;  // sum of (stored activation) * (its bias weight)
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS);
+        u32x4_t o;
 #pragma unroll
-        for (int q = 0; q < GS / 8; ++q) {
-            u32x4_t o;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
-                const int k0 = frag_src(BITS, GS, p0), k1 = frag_src(BITS, GS, p1);
-                const uint32_t lo =
-                    bf16_scaled((w[k0 >> 1] >> (16 * (k0 & 1))) & 0xffffu, frag_shift(BITS, GS, p0));
-                const uint32_t hi =
-                    bf16_scaled((w[k1 >> 1] >> (16 * (k1 & 1))) & 0xffffu, frag_shift(BITS, GS, p1));
-                sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
-                sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
-                o[h] = lo | (hi << 16);
-            }
-            dst[q] = o;
+        for (int h = 0; h < 4; ++h) {
+            const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
+            const uint32_t lo = bf16_scaled(e[2 * h], frag_shift(BITS, GS, p0));
+            const uint32_t hi = bf16_scaled(e[2 * h + 1], frag_shift(BITS, GS, p1));
+            sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
+            sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
+            o[h] = lo | (hi << 16);
         }
-        ws.x_bias[(size_t)t * ngroups + G] = -sum;   // stored negated: the chain start
+#pragma unroll
+        for (int m = 1; m < PL; m <<= 1)
+            sum += __shfl_xor(sum, m, 64);
+        if (on) {
+            reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS)[q] = o;
+            if (q == 0)
+                ws.x_bias[(size_t)t * ngroups + G] = -sum;   // stored negated: the chain start
+        }
         return;
     }
     // zero the accumulator and the act bias terms (the decode epilogue adds into them)
@@ -1646,7 +1644,7 @@ template <int BITS, int GS>
 static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims &d,
                           const Workspace &ws, hipStream_t stream, const KernelEvents &ev)
 {
-    const long nthreads_prep = (long)d.T * (d.H / GS);
+    const long nthreads_prep = (long)d.T * (d.H / 8);   // 8 fragment positions per thread
     const int nprep = (int)((nthreads_prep + kAlignThreads - 1) / kAlignThreads);
     const long n4 = (long)d.T * d.H / 4;
     long nzero = (n4 + 4L * kAlignThreads - 1) / (4L * kAlignThreads);
