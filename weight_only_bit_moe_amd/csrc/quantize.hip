@@ -12,7 +12,9 @@
 //   amax  by a butterfly over the group's lanes (DPP, no LDS);
 //   s0 = amax / ((2^b - 1) / 2) (FP32 division);
 //   for each candidate c: s_c = fp16_rne(min(s0 * f_c, 65504)),
-//     f_c = 1 - c / (2C); error sum_k imp_k (w_k - s_c q_k)^2 in FP64;
+//     f_c = 1 - c / (2C); error sum_k imp_k (w_k - s_c q_k)^2 in FP64, formed
+//     as sum_k (sqrt(imp_k) d_k)^2 with one fma per weight (only the last-bit
+//     rounding differs from imp * d * d, so only near-ties can rank apart);
 //   the smallest error wins, ties to the smaller c;
 //   the winner's codes q = clamp(rne(w / s)) by FP32 division, packed with the
 //   least-significant field first as u = q + 2^(b-1): a lane's 16 codes fill
@@ -122,10 +124,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
     const size_t row_vecs = (size_t)K / 8;
     const int kw = K * BITS / 32, ng = K / GS;
 
-    double im[kQEpl];
+    double im[kQEpl], rim[kQEpl];   // importance and its square root (FP64)
 #pragma unroll
-    for (int i = 0; i < kQEpl; ++i)
+    for (int i = 0; i < kQEpl; ++i) {
         im[i] = (IMP && on) ? (double)imp[k0 + i] : 1.0;
+        rim[i] = __builtin_sqrt(im[i]);
+    }
     double a_err = 0.0, a_w2 = 0.0, a_ierr = 0.0, a_iw2 = 0.0;
 
     uint4 va = make_uint4(0, 0, 0, 0), vb = va;
@@ -173,7 +177,10 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             for (int i = 0; i < kQEpl; ++i) {
                 const float q = __builtin_amdgcn_fmed3f(rintf(x[i] * rs), qlo, qhi);
                 const double d = __builtin_fma(ns, (double)q, wd[i]);
-                e += IMP ? (im[i] * d) * d : d * d;
+                // the search compares candidates: (sqrt(imp) d)^2 summed with
+                // one fma, two FP64 operations instead of three
+                const double t = IMP ? rim[i] * d : d;
+                e = __builtin_fma(t, t, e);
             }
             e = seg_sum<L>(e);
             if (c == 0 || e < best) {
