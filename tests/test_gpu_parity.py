@@ -150,6 +150,13 @@ SMALL = {
     # 64 and 48 groups per row: the scale/bias staging runs in two segments
     "pre_g32_two_segments": (spec(T=48, H=2048, I=1536, E=3, topk=2, bits13=4, group13=32,
                                   bits2=2, group2=32, **ACT), None, PRE),
+    # the documented maximums: 1024 experts, top-64 (every expert of a token)
+    "dec_max_experts": (spec(T=16, H=256, I=128, E=1024, topk=8), None, DEC),
+    "dec_max_topk": (spec(T=4, H=256, I=128, E=64, topk=64, **ACT), None, DEC),
+    "pre_max_experts": (spec(T=1024, H=256, I=128, E=1024, topk=8, bits13=2, bits2=2),
+                        None, PRE),
+    "pre_max_topk": (spec(T=40, H=256, I=128, E=64, topk=64, group13=64, group2=32),
+                     None, PRE),
     # H = 640: the last w2 column block is partly idle (640 = 512 + 128)
     "pre_w2_partial_column_block": (spec(T=64, H=640, I=384, E=3, topk=2, bits13=2,
                                          group13=64, bits2=4, group2=128), None, PRE),
