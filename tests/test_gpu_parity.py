@@ -150,6 +150,11 @@ SMALL = {
     # 64 and 48 groups per row: the scale/bias staging runs in two segments
     "pre_g32_two_segments": (spec(T=48, H=2048, I=1536, E=3, topk=2, bits13=4, group13=32,
                                   bits2=2, group2=32, **ACT), None, PRE),
+    # degenerate shapes: one expert over several 64-row tiles, and the
+    # smallest hidden and intermediate sizes (128)
+    "pre_single_expert_4_tiles": (spec(T=200, H=256, I=128, E=1, topk=1, **ACT), None, PRE),
+    "dec_min_hidden": (spec(T=3, H=128, I=128, E=4, topk=2), None, DEC),
+    "pre_min_hidden": (spec(T=70, H=128, I=128, E=2, topk=2, bits13=2, bits2=2), None, PRE),
     # the documented maximums: 1024 experts, top-64 (every expert of a token)
     "dec_max_experts": (spec(T=16, H=256, I=128, E=1024, topk=8), None, DEC),
     "dec_max_topk": (spec(T=4, H=256, I=128, E=64, topk=64, **ACT), None, DEC),
