@@ -193,7 +193,7 @@ int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t 
  * and the smallest err_c wins (ties to the smaller c); C = n_candidates, so
  * C = 1 is plain round-to-nearest with the absmax scale.
  *
- *   w           [rows, K] bf16, row-major                        4-byte aligned
+ *   w           [rows, K] bf16, row-major                       16-byte aligned
  *   imp         [K] float32 importance per input channel (>= 0), or NULL for
  *               all ones (the unweighted search)                 4-byte aligned
  *   codes_out   [rows, K*b/32] int32 in the packed format above  4-byte aligned

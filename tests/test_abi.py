@@ -161,6 +161,7 @@ def test_quantize_rejects(lib):
     assert call(w=0) == Bd.EINVAL
     assert call(err_sums_out=0) == Bd.EINVAL
     assert call(w=258) == Bd.EALIGN
+    assert call(w=260) == Bd.EALIGN          # weights are read 16 bytes at a time
     assert call(imp=258) == Bd.EALIGN
     assert call(err_sums_out=260) == Bd.EALIGN
     assert call(scales_out=257) == Bd.EALIGN

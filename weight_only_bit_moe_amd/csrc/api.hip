@@ -402,9 +402,9 @@ int moe_wna16_quantize(const void *w, const float *imp, int rows, int K, moe_wna
         return MOE_WNA16_EUNSUPPORTED;
     if ((rows > 0 && (!w || !codes_out || !scales_out)) || !err_sums_out)
         return MOE_WNA16_EINVAL;
-    if (!aligned(w, 4) || !aligned(imp, 4) || !aligned(codes_out, 4) ||
+    if (!aligned(w, 16) || !aligned(imp, 4) || !aligned(codes_out, 4) ||
         !aligned(scales_out, 2) || !aligned(err_sums_out, 8))
-        return MOE_WNA16_EALIGN;
+        return MOE_WNA16_EALIGN;   // weights are read 16 bytes at a time
     const int st = check_device();
     if (st != MOE_WNA16_OK)
         return st;
