@@ -68,10 +68,18 @@ def _align_cases():
     cases.append(("bad_ids_multi_block", rng.integers(-3, 20, size=(3000, 4)), 16))
     cases.append(("exact_two_chunks", rng.integers(0, 64, size=(1024, 8)), 64))
     cases.append(("chunk_plus_one", rng.integers(0, 8, size=(4097, 1)), 8))
+    # up to 64 pairs: one wave sorts them (no workgroup barriers)
+    for i, (T, k, E) in enumerate([(1, 1, 1), (4, 6, 256), (8, 8, 1024), (3, 7, 1000),
+                                   (16, 4, 8), (64, 1, 3), (2, 5, 64)]):
+        cases.append((f"wave_fuzz{i}", rng.integers(0, E, size=(T, k)), E))
+    cases.append(("wave_bad_ids", rng.integers(-3, 20, size=(15, 4)), 16))
+    cases.append(("wave_all_bad", np.full((4, 6), 300), 256))
+    cases.append(("wave_one_expert_64", np.full((64, 1), 5), 8))
+    cases.append(("wave_65_pairs", rng.integers(0, 4, size=(13, 5)), 4))   # block path
     return cases
 
 
-@pytest.mark.parametrize("bm", [1, 16, 64, 128])
+@pytest.mark.parametrize("bm", [1, 4, 16, 64, 128])
 @pytest.mark.parametrize("case", range(len(_align_cases())))
 def test_align_bit_exact(dev, case, bm):
     name, ids, E = _align_cases()[case]

@@ -238,6 +238,89 @@ __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, in
     }
 }
 
+// Up to this many pairs, the first wave of the sort workgroup sorts them on
+// its own (align_wave) and the other waves leave at once.
+constexpr int kWaveSortPairs = 64;
+
+// Orders LDS accesses of different lanes of one wave (a wave's LDS
+// instructions complete in issue order; this keeps the compiler from moving
+// them across and waits for the outstanding ones).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The stable expert sort of P <= 64 pairs by one wave (lane p holds pair p),
+// with the same results as align_block.  A pair's rank among the pairs of its
+// expert is the number of earlier lanes holding the same id (the ballot match
+// of align_block); the first of them (the leader) records the expert's padded
+// count in LDS and later writes the expert's tiles and padding slots.  The
+// expert offsets are a wave-level exclusive scan over per-lane runs of
+// ceil(E / 64) consecutive experts.  No workgroup barrier is needed.
+__device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int P, int E, int bm,
+                           int32_t *__restrict__ sorted_ids, int32_t *__restrict__ tile_expert,
+                           int32_t *__restrict__ offsets, int32_t *__restrict__ inv_perm,
+                           int32_t *__restrict__ num_tiles, int32_t *__restrict__ bad_ids)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int e = lane < P ? ids[lane] : -1;
+    const bool ok = lane < P && e >= 0 && e < E;
+    const uint64_t m = match_key(ok ? e : kMaxExperts);   // invalid lanes share one key
+    const int rank = __popcll(m & below);
+    const bool leader = ok && (m & below) == 0;
+    const int cnt = __popcll(m);
+    const int padded = (cnt + bm - 1) / bm * bm;
+    const int nbad = __popcll(__ballot(lane < P && !ok));
+
+    for (int i = lane; i < E; i += 64)
+        sh.cnt[i] = 0;
+    wave_lds_sync();
+    if (leader)
+        sh.cnt[e] = padded;
+    wave_lds_sync();
+    const int per = (E + 63) / 64;
+    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+    int run = 0;
+    for (int i = e0; i < e1; ++i)
+        run += sh.cnt[i];
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += y;
+    }
+    int acc = incl - run;
+    for (int i = e0; i < e1; ++i) {
+        const int c = sh.cnt[i];
+        sh.off[i] = acc;
+        offsets[i] = acc;
+        acc += c;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (lane == 0) {
+        offsets[E] = total;
+        *num_tiles = total / bm;
+        *bad_ids = nbad;
+    }
+    wave_lds_sync();
+    if (ok) {
+        const int base = sh.off[e];
+        sorted_ids[base + rank] = lane;
+        inv_perm[lane] = base + rank;
+        if (leader) {
+            for (int s = base + cnt; s < base + padded; ++s)
+                sorted_ids[s] = P;
+            for (int t = base / bm; t < (base + padded) / bm; ++t)
+                tile_expert[t] = e;
+        }
+    } else if (lane < P) {
+        inv_perm[lane] = -1;
+    }
+}
+
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t *__restrict__ ids, int P, int E, int bm, int32_t *__restrict__ sorted_ids,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
@@ -245,6 +328,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     int32_t *__restrict__ bad_ids)
 {
     __shared__ AlignShared sh;
+    if (P <= kWaveSortPairs) {
+        if (threadIdx.x < 64)
+            align_wave(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
+                       bad_ids);
+        return;
+    }
     align_block(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
                 bad_ids, blockIdx.x, gridDim.x);
 }
@@ -288,6 +377,12 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     __shared__ AlignShared sh;
     const int blk = blockIdx.x;
     if (blk < nalign) {
+        if (T * topk <= kWaveSortPairs) {
+            if (threadIdx.x < 64)
+                align_wave(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert,
+                           ws.expert_offsets, ws.inv_perm, ws.meta, ws.meta + 1);
+            return;
+        }
         align_block(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert, ws.expert_offsets,
                     ws.inv_perm, ws.meta, ws.meta + 1, blk, nalign,
                     nalign >= kCountedSortBlocks ? ws.chunk_counts : nullptr);
