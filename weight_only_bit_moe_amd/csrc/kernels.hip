@@ -1288,17 +1288,18 @@ struct Stream {
                                                         f32x4_t (&acc)[NB])
     {
         bf16x8_t af[GPU][S];
-        f32x4_t negb[GPU];
+        float negb[GPU];
         float sc[GPU][NB];
-        const uint16_t *arow = sA + (c < R ? c : R) * lds_stride;
+        // tile row r is MFMA row 4r, so result lane group g holds row g in
+        // element 0; the other MFMA rows read the zero row
+        const uint16_t *arow = sA + ((c & 3) == 0 ? (c >> 2) : R) * lds_stride;
 #pragma unroll
         for (int gq = 0; gq < GPU; ++gq) {
             const int G = u * GPU + gq;
 #pragma unroll
             for (int s = 0; s < S; ++s)
                 af[gq][s] = *reinterpret_cast<const bf16x8_t *>(arow + G * GS + (s * 4 + g) * 8);
-            // rows 0..R-1 sit in lane group 0; other lanes read the zero block
-            negb[gq] = *reinterpret_cast<const f32x4_t *>(sBias + (g == 0 ? G * R : ngroups * R));
+            negb[gq] = sBias[G * R + g];   // row g's chain start
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 sc[gq][j] = f16_to_f32(sSw[(j * 16 + c) * ngroups + G]);
@@ -1327,14 +1328,14 @@ struct Stream {
                     const bf16x8_t bf = unpack<BITS, GS, NDW>(
                         reinterpret_cast<const uint32_t(&)[NDW]>(cw), s, g, magic);
                     accg[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        af[gq][s], bf, s == 0 ? negb[gq] : accg[j], 0, 0, 0);
+                        af[gq][s], bf, s == 0 ? f32x4_t{negb[gq], 0.f, 0.f, 0.f} : accg[j],
+                        0, 0, 0);
                 }
             }
+            // only element 0 holds a tile row
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    acc[j][v] = fmaf(sc[gq][j], accg[j][v], acc[j][v]);
+                acc[j][0] = fmaf(sc[gq][j], accg[j][0], acc[j][0]);
         }
     }
 
@@ -1566,7 +1567,8 @@ struct Stream {
             compute_unit(q[d], u0 + d, sA, sBias, sSw, lds_stride, ngroups, c, g, magic, acc);
         }
 
-        // rows 0..3 of every subtile live in lane group 0, element v = row
+        // tile row g of every subtile lives in lane group g, element 0
+        static_assert(R == 4, "one tile row per lane group");
         if constexpr (W13) {
             constexpr int NG = NB / 2;
             const int gs2 = args.gs_next, bits2 = args.bits_next;
@@ -1579,27 +1581,24 @@ struct Stream {
                 const int pos = G2 * gs2 + pin;
                 const int esh = frag_shift(bits2, gs2, pin);
                 const float wgt = (float)frag_bias_weight(bits2, gs2, pin);
-#pragma unroll
-                for (int v = 0; v < R; ++v) {
-                    float a = 0.f;
-                    if (g == 0 && v < rows_real) {
-                        a = swiglu(acc[j][v], acc[NG + j][v], args.alpha, args.beta, args.clamp);
-                        const uint32_t st = bf16_scaled(f32_to_bf16(a), esh);
-                        uint16_t *dst = args.act_out + (size_t)(b * R + v) * args.N + pos;
-                        if constexpr (FUSED)   // read by w2 workgroups of this launch
-                            __hip_atomic_store(dst, (uint16_t)st, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                        else
-                            *dst = (uint16_t)st;
-                        a = bf16_to_f32(st) * wgt;
-                    }
-                    // sum of the 16 columns of this subtile (lanes 0..15)
-#pragma unroll
-                    for (int m = 1; m < 16; m <<= 1)
-                        a += __shfl_xor(a, m, 64);
-                    if (lane == 0)
-                        s_part[v][wave * NG + j] = a;
+                float a = 0.f;
+                if (g < rows_real) {
+                    a = swiglu(acc[j][0], acc[NG + j][0], args.alpha, args.beta, args.clamp);
+                    const uint32_t st = bf16_scaled(f32_to_bf16(a), esh);
+                    uint16_t *dst = args.act_out + (size_t)(b * R + g) * args.N + pos;
+                    if constexpr (FUSED)   // read by w2 workgroups of this launch
+                        __hip_atomic_store(dst, (uint16_t)st, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *dst = (uint16_t)st;
+                    a = bf16_to_f32(st) * wgt;
                 }
+                // sum of the 16 columns of this subtile (the lanes of group g)
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1)
+                    a += __shfl_xor(a, m, 64);
+                if (c == 0)
+                    s_part[g][wave * NG + j] = a;
             }
             __syncthreads();
             // one partial sum per (row, w2 group) inside this workgroup; a group
@@ -1625,18 +1624,13 @@ struct Stream {
                                            __HIP_MEMORY_SCOPE_AGENT);
             }
         } else {
-            if (g == 0) {
+            if (g < rows_real) {
+                const int p = g == 0 ? pair[0] : g == 1 ? pair[1] : g == 2 ? pair[2] : pair[3];
+                const float w = args.topk_w[p];
+                float *orow = args.out_f32 + (size_t)(p / args.topk) * args.N;
 #pragma unroll
-                for (int v = 0; v < R; ++v) {
-                    if (v >= rows_real)
-                        continue;
-                    const int p = pair[v];
-                    const float w = args.topk_w[p];
-                    float *orow = args.out_f32 + (size_t)(p / args.topk) * args.N;
-#pragma unroll
-                    for (int j = 0; j < NB; ++j)
-                        unsafeAtomicAdd(orow + nb * BN + wave * COLS + j * 16 + c, w * acc[j][v]);
-                }
+                for (int j = 0; j < NB; ++j)
+                    unsafeAtomicAdd(orow + nb * BN + wave * COLS + j * 16 + c, w * acc[j][0]);
             }
             if (args.out_bf16)
                 arrive(args, ntiles, nb);
