@@ -61,6 +61,9 @@ CASES = {
     "w4g32_one_launch": spec(T=5, H=512, I=256, E=6, topk=2, group13=32, group2=32),
     "w2g64_one_launch": spec(T=3, H=1024, I=512, E=4, topk=2, bits13=2, bits2=2, group13=64,
                              group2=64),
+    # 2-bit g128, K of 2048 on both projections (several pipeline rounds)
+    "w2g128_k2048_one_launch": spec(T=4, H=2048, I=2048, E=8, topk=3, bits13=2, bits2=2),
+    "w2g128_w4g128_down": spec(T=5, H=2048, I=1024, E=8, topk=2, bits13=2, bits2=4, **ACT),
     # separate launches (formats differ, or 2-bit group 32)
     "w4g128_w2g64": spec(T=8, H=512, I=512, E=16, topk=4, bits2=2, group2=64, **ACT),
     "w2g32_w4g32": spec(T=6, H=512, I=256, E=8, topk=2, bits13=2, group13=32, group2=32),
