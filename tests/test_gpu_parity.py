@@ -133,6 +133,11 @@ SMALL = {
                               None, DEC),
     "dec_w2g128_long_k": (spec(T=4, H=2048, I=1024, E=8, topk=3, bits13=2, bits2=2,
                                scale_lo=0.01, scale_hi=0.05), None, DEC),
+    # the route kernel sorts up to 64 pairs on one wave, more on a workgroup
+    "dec_64_pairs_one_wave_sort": (spec(T=8, H=1024, I=1024, E=16, topk=8, bits13=2, bits2=2),
+                                   None, DEC),
+    "dec_65_pairs_workgroup_sort": (spec(T=13, H=256, I=256, E=20, topk=5, bits13=2, bits2=2),
+                                    None, DEC),
     "dec_3_4_5_rows": (spec(T=12, H=256, I=128, E=8, topk=2), "345", DEC),
     # 2-bit codes with K an odd multiple of 128: the tile kernel takes these
     # small batches (the decode kernels need K in units of 256)
