@@ -162,8 +162,11 @@ def main():
 
     cfg = args.config
     decode = cfg in (2, 3)
-    steps = args.steps if args.steps is not None else (200 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    # Decode steps are ~40 us: a few hundred untimed calls bring the host's
+    # enqueue path and the clocks to steady state (after 20 the launches of
+    # one step were still ~3 us apart).
+    steps = args.steps if args.steps is not None else (1000 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (500 if decode else 10)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
