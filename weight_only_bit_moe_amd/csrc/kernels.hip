@@ -1195,7 +1195,7 @@ struct Stream {
     // dynamic LDS: A rows, their group bias terms, the workgroup's scales
     static __host__ __device__ size_t lds_bytes(int K)
     {
-        return (size_t)(R + 1) * (K + 8) * 2 + ((size_t)R * (K / GS) + 4) * 4 +
+        return (size_t)(R + 1) * (K + 8) * 2 + (size_t)R * (K / GS) * 4 +
                (size_t)NW * NB * 16 * (K / GS) * 2;
     }
 
@@ -1339,17 +1339,16 @@ struct Stream {
         }
     }
 
-    // Negated bias term (stored negated) of LDS item i ([group][row], then 4
-    // zeros): the start of each MFMA chain.
+    // Negated bias term (stored negated) of LDS item i = [group][row]: the
+    // start of each MFMA chain (0 for padding rows).
     static constexpr int NBIAS_PRE = 2;
     static __device__ __forceinline__ float bias_item(const GemmArgs &args, int s0, int s1, int s2,
                                                       int s3, int i, int ngroups)
     {
         static_assert(R == 4, "four tile rows");
         const int G = i / R, r = i % R;
-        int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
-        sr = i < R * ngroups ? sr : -1;
-        const float *bp = args.a_bias + (size_t)(sr >= 0 ? sr : 0) * ngroups + (G < ngroups ? G : 0);
+        const int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
+        const float *bp = args.a_bias + (size_t)(sr >= 0 ? sr : 0) * ngroups + G;
         float bv;
         if constexpr (FUSED && !W13)   // written by this launch's w13 items
             bv = __hip_atomic_load(bp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1395,11 +1394,11 @@ struct Stream {
         const int ngroups = K / GS;
         const int lds_stride = K + 8;
         // LDS: R activation rows + a zero row; the rows' negated bias terms as
-        // [group][row] + 4 zeros; the workgroup's scales
+        // [group][row]; the workgroup's scales
         uint16_t *sA = reinterpret_cast<uint16_t *>(smem);
         float *sBias = reinterpret_cast<float *>(smem + (size_t)(R + 1) * lds_stride * 2);
         uint16_t *sS = reinterpret_cast<uint16_t *>(smem + (size_t)(R + 1) * lds_stride * 2 +
-                                                    ((size_t)R * ngroups + 4) * 4);
+                                                    (size_t)R * ngroups * 4);
         __shared__ float s_part[R][NW * (W13 ? NB / 2 : 1)];
 
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1462,7 +1461,7 @@ struct Stream {
 #pragma unroll
         for (int k = 0; k < NBIAS_PRE; ++k) {
             const int i = tid + k * NTHREADS;
-            bpre[k] = i < R * ngroups + 4 ? bias_item(args, src[0], src[1], src[2], src[3], i, ngroups)
+            bpre[k] = i < R * ngroups ? bias_item(args, src[0], src[1], src[2], src[3], i, ngroups)
                                           : 0.f;
         }
         {
@@ -1511,14 +1510,14 @@ struct Stream {
                             vs[t];
                 }
             }
-            for (int i = tid; i < R * ngroups + 4; i += NTHREADS) {
+            for (int i = tid; i < R * ngroups; i += NTHREADS) {
                 if (i < NBIAS_PRE * NTHREADS)
                     continue;   // staged from the batch loaded above
                 sBias[i] = bias_item(args, src[0], src[1], src[2], src[3], i, ngroups);
             }
 #pragma unroll
             for (int k = 0; k < NBIAS_PRE; ++k)
-                if (tid + k * NTHREADS < R * ngroups + 4)
+                if (tid + k * NTHREADS < R * ngroups)
                     sBias[tid + k * NTHREADS] = bpre[k];
             if (!svec) {   // scales without 16-byte alignment: one half at a time
                 for (int i = tid; i < srows * ngroups; i += NTHREADS) {
