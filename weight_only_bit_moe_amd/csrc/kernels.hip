@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t bf16_scaled(uint32_t h, int e)
 // ---------------------------------------------------------------------------
 // Stable expert sort of the pairs, on one or more workgroups of 1024 threads.
 //
-// Workgroup w places the pairs [w*kAlignChunk, (w+1)*kAlignChunk).  Every
+// Workgroup w places the pairs [w*chunk, (w+1)*chunk).  Every
 // workgroup first counts all pairs per expert (the padded exclusive scan of
 // those counts gives the expert offsets) and, separately, the pairs before
 // its own range; its pairs of expert e then start at offset[e] + (pairs of e
@@ -102,13 +102,13 @@ __device__ void align_block(AlignShared &sh, const int32_t *__restrict__ ids, in
                             int bm, int32_t *__restrict__ sorted_ids,
                             int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
                             int32_t *__restrict__ inv_perm, int32_t *__restrict__ num_tiles,
-                            int32_t *__restrict__ bad_ids, int blk, int nblk,
+                            int32_t *__restrict__ bad_ids, int blk, int nblk, int chunk,
                             const int32_t *__restrict__ chunk_counts = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int NW = kAlignThreads / 64;
-    const int begin = blk * kAlignChunk;
-    const int end = min(P, begin + kAlignChunk);
+    const int begin = blk * chunk;
+    const int end = min(P, begin + chunk);
     for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
         sh.cnt[e] = 0;
         sh.pre[e] = 0;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t *__restrict__ ids, int P, int E, int bm, int32_t *__restrict__ sorted_ids,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
     int32_t *__restrict__ inv_perm, int32_t *__restrict__ num_tiles,
-    int32_t *__restrict__ bad_ids)
+    int32_t *__restrict__ bad_ids, int chunk)
 {
     __shared__ AlignShared sh;
     if (P <= kWaveSortPairs) {
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
         return;
     }
     align_block(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
-                bad_ids, blockIdx.x, gridDim.x);
+                bad_ids, blockIdx.x, gridDim.x, chunk);
 }
 
 // From this many sort workgroups on, the route kernel's sort takes its
@@ -348,13 +348,13 @@ inline int align_blocks(int P) { return align_chunks(P); }
 // Per-chunk expert counts (and invalid ids, in entry E) for the multi-
 // workgroup sort inside the route kernel.
 __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
-    const int32_t *__restrict__ ids, int P, int E, int32_t *__restrict__ counts)
+    const int32_t *__restrict__ ids, int P, int E, int chunk, int32_t *__restrict__ counts)
 {
     __shared__ int hist[kMaxExperts + 1];
     for (int e = threadIdx.x; e <= E; e += kAlignThreads)
         hist[e] = 0;
     __syncthreads();
-    const int begin = blockIdx.x * kAlignChunk, end = min(P, begin + kAlignChunk);
+    const int begin = blockIdx.x * chunk, end = min(P, begin + chunk);
     for (int p = begin + threadIdx.x; p < end; p += kAlignThreads) {
         const int e = ids[p];
         atomicAdd(&hist[(e >= 0 && e < E) ? e : E], 1);
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
 template <int BITS, int GS>
 __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ ids, int T, int H, int topk,
-    int E, int bm, int nalign, int nprep, size_t act_bias_n, int tdone_n, Workspace ws)
+    int E, int bm, int nalign, int chunk, int nprep, size_t act_bias_n, int tdone_n, Workspace ws)
 {
     __shared__ AlignShared sh;
     const int blk = blockIdx.x;
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
             return;
         }
         align_block(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert, ws.expert_offsets,
-                    ws.inv_perm, ws.meta, ws.meta + 1, blk, nalign,
+                    ws.inv_perm, ws.meta, ws.meta + 1, blk, nalign, chunk,
                     nalign >= kCountedSortBlocks ? ws.chunk_counts : nullptr);
         return;
     }
@@ -1724,7 +1724,7 @@ hipError_t launch_align(const int32_t *topk_ids, int T, int topk, int E, int blo
     hipLaunchKernelGGL(align_kernel, dim3(align_blocks(T * topk)), dim3(kAlignThreads), 0, stream,
                        topk_ids,
                        T * topk, E, block_m, sorted_ids, tile_expert, expert_offsets, inv_perm,
-                       num_tiles, bad_ids);
+                       num_tiles, bad_ids, align_chunk(T * topk));
     return hipGetLastError();
 }
 
@@ -1741,18 +1741,20 @@ static hipError_t route_t(const uint16_t *x, const int32_t *ids, const LayerDims
     if (nzero > 1024)
         nzero = 1024;
     const int nalign = align_blocks(d.T * d.topk);
+    const int chunk = align_chunk(d.T * d.topk);
     // With many sort workgroups, each one recounting every pair costs more
     // than one extra launch: count per chunk first, the sort sums the counts.
     const bool counted = nalign >= kCountedSortBlocks;
     hipEvent_t route_start = ev.start;
     if (counted) {
         hipExtLaunchKernelGGL(align_count_kernel, dim3(nalign), dim3(kAlignThreads), 0, stream,
-                              ev.start, nullptr, 0, ids, d.T * d.topk, d.E, ws.chunk_counts);
+                              ev.start, nullptr, 0, ids, d.T * d.topk, d.E, chunk,
+                              ws.chunk_counts);
         route_start = nullptr;
     }
     hipExtLaunchKernelGGL((route_kernel<BITS, GS>), dim3(nalign + nprep + (int)nzero),
                           dim3(kAlignThreads), 0, stream, route_start, ev.stop, 0, x, ids, d.T, d.H,
-                          d.topk, d.E, d.block_m, nalign, nprep,
+                          d.topk, d.E, d.block_m, nalign, chunk, nprep,
                           // only the decode-shaped w13 adds into act_bias
                           d.variant13 == 2 ? (size_t)d.max_tiles * d.block_m * (d.I / d.g2) : 0,
                           d.max_tiles * 16, ws);

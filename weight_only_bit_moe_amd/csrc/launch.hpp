@@ -26,8 +26,22 @@ struct Workspace {
 };
 
 // Pairs per workgroup of the expert sort.
-constexpr int kAlignChunk = 4096;
-inline int align_chunks(long long P) { return P <= kAlignChunk ? 1 : (int)((P + kAlignChunk - 1) / kAlignChunk); }
+// Pairs per sort workgroup: a multiple of 1024 (one placement step), the
+// smallest that keeps the sort at most kMaxSortBlocks workgroups (each one
+// reads the counts of every chunk).
+constexpr int kAlignStep = 1024;
+constexpr int kMaxSortBlocks = 16;
+inline int align_chunk(long long P)
+{
+    const long long per = (P + kMaxSortBlocks - 1) / kMaxSortBlocks;
+    const long long c = (per + kAlignStep - 1) / kAlignStep * kAlignStep;
+    return (int)(c < kAlignStep ? kAlignStep : c);
+}
+inline int align_chunks(long long P)
+{
+    const long long c = align_chunk(P);
+    return P <= c ? 1 : (int)((P + c - 1) / c);
+}
 
 // Optional start/stop events recorded by the kernel dispatch itself
 // (hipExtLaunchKernelGGL); null events record nothing.
