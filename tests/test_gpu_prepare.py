@@ -11,7 +11,7 @@ import weight_only_bit_moe_amd as M
 from oracle import oracle as O
 from tests import _gpu as G
 from weight_only_bit_moe_amd import binding as Bd
-from weight_only_bit_moe_amd.inputs import LayerSpec, make_config, make_layer
+from weight_only_bit_moe_amd.inputs import LayerSpec, make_batch, make_config, make_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,32 @@ def test_forward_prepared_full_workload_sampled_tokens(dev, cfg):
     assert np.all(np.isfinite(y))
     rows = [0, 1, L.spec.T - 1] if L.spec.T > 3 else list(range(L.spec.T))
     G.assert_parity(y[rows], O.forward_layer(L, tokens=rows), f"config {cfg} prepared")
+
+
+def test_forward_prepared_new_batches_on_one_workspace(dev):
+    """Codes prepared once, then calls with a new routing batch each on one
+    workspace and one output buffer (the shared decode launch with the fused
+    rounding): every call matches the oracle."""
+    sp = spec(T=4, H=1024, I=1024, E=16, topk=4, bits13=2, bits2=2)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (2, 128), (2, 128))
+    assert plan["gemms_one_launch"] == 1 and plan["convert_in_w2"] == 1
+    L = make_layer(sp, seed=77)
+    d = G.to_device(L, dev)
+    w13 = M.prepare(d["w13"], sp.bits13, sp.group13)
+    w2 = M.prepare(d["w2"], sp.bits2, sp.group2)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    out = torch.empty((sp.T, sp.H), dtype=torch.bfloat16, device=dev)
+    for rep in range(5):
+        ids, w, x = make_batch(sp, seed=500 + rep)
+        y = M.forward(torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16),
+                      torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev), w13, d["s13"],
+                      w2, d["s2"], bits=(sp.bits13, sp.bits2), group=(sp.group13, sp.group2),
+                      alpha=sp.alpha, beta=sp.beta, clamp=None, out=out, workspace=ws,
+                      prepared=True)
+        torch.cuda.synchronize(dev)
+        Lr = make_layer(sp, seed=77, topk_ids=ids)
+        Lr.topk_w, Lr.x = w, x
+        G.assert_parity(G.to_f64(y), O.forward_layer(Lr), f"batch {rep}")
 
 
 def test_forward_prepared_rejects_prefill_shapes(dev):
