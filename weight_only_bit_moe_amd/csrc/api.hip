@@ -64,7 +64,7 @@ Layout layout_of(int T, int H, int I, int E, int topk)
         o = round_up(o + bytes, kRegionAlign);
         return at;
     };
-    L.meta = take(2 * sizeof(int32_t));
+    L.meta = take((8 + 2 * wna16::kSplitEntries) * sizeof(int32_t));   // counts, then the XCD split
     L.offsets = take((size_t)(E + 1) * sizeof(int32_t));
     L.sorted = take(max_slots * sizeof(int32_t));
     L.tiles = take(max_tiles * sizeof(int32_t));
@@ -268,6 +268,7 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.chunk_counts = reinterpret_cast<int32_t *>(base + L.ccounts);
     ws.done = reinterpret_cast<int32_t *>(base + L.done);
     ws.tile_done = reinterpret_cast<int32_t *>(base + L.tdone);
+    ws.xcd_first = ws.meta + 8;
 
     wna16::KernelEvents ev[4];
     if (events)
@@ -276,6 +277,9 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, ev[0]))) !=
         MOE_WNA16_OK)
+        return st;
+    if ((plan.w13_variant == 1 || plan.w2_variant == 1) &&
+        (st = hip_status(wna16::launch_split(d, ws, stream))) != MOE_WNA16_OK)
         return st;
     // Small outputs: the last decode w2 workgroup of each column block rounds
     // that block to BF16, which saves the convert launch.  Decode shapes whose

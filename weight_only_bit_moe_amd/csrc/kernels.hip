@@ -470,6 +470,7 @@ struct GemmArgs {
     int bits_next, gs_next;   // W13 epilogue: format of the w2 operand
     float alpha, beta, clamp;
     int prepared;             // codes in the prepared block order (decode-shaped kernels only)
+    const int32_t *xcd_first; // tile kernel: [9] first item of each XCD's range, then the total
 };
 
 template <int BITS, int GS>
@@ -936,13 +937,12 @@ struct Tile {
         cx.g = cx.lane >> 4;
         const int tid = cx.tid, lane = cx.lane;
 
-        // (tile, column block) item of this workgroup
+        // (tile, column block) item of this workgroup: the jx-th of its XCD's
+        // contiguous range (split_kernel balances the ranges' MFMA work)
         const int nblk = (args.N + OUTC - 1) / OUTC;
-        const int total = *args.num_tiles * nblk;
-        const int per = (total + kXcds - 1) / kXcds;
         const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
-        const int item = xcd * per + jx;
-        if (jx >= per || item >= total)
+        const int item = args.xcd_first[xcd] + jx;
+        if (item >= args.xcd_first[xcd + 1])
             return;
         cx.b = item / nblk;
         cx.nb = item % nblk;
@@ -1776,6 +1776,119 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
     }
 }
 
+// Workgroup slots per XCD of a tile-kernel launch: room for a split of up to
+// max_tiles tiles whose longest range is 1.5 times the even share plus a tile.
+static int tile_xcd_cap(int max_tiles, int N, bool w13)
+{
+    const int outc = w13 ? Tile<2, 128, true>::OUTC : Tile<2, 128, false>::OUTC;
+    const long nblk = (N + outc - 1) / outc;
+    const long per = ((long)max_tiles * nblk + 7) / 8;
+    return (int)(per + per / 2 + nblk);
+}
+
+// Relative cost of one tile-kernel item: a fixed part (its expert's codes are
+// copied and unpacked whatever the row count) plus the MFMA chains of its
+// active 16-row slices, weighted 3 : 1 (measured best among 1 : 2, 2 : 1,
+// 3 : 1 and 5 : 1 on 2048- and 8192-token Zipf-routed batches).  Padding
+// slots sit at the end of a tile and hold P.
+__device__ __forceinline__ int split_tile_cost(const int32_t *sorted_ids, int b, int P)
+{
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        n += sorted_ids[b * 64 + 16 * s] < P ? 1 : 0;
+    return 3 + n;
+}
+
+// Cost-balanced split of the tile kernel's (tile, column block) items over
+// the 8 XCDs.  Each XCD keeps a contiguous, tile-major range (the L2 reuse of
+// activations and expert codes stays), and range x starts at the first item
+// whose preceding cost reaches x/8 of the total.  Every range is then capped
+// at `cap` items, the workgroup slots the launch gives each XCD; since
+// 8 * cap >= the item count, the capped ranges still cover every item once.
+// One workgroup; writes first[9] for w13, then first[9] for w2.
+__global__ __launch_bounds__(1024) void split_kernel(const int32_t *__restrict__ sorted_ids,
+                                                     const int32_t *__restrict__ meta, int P,
+                                                     int nblk13, int cap13, int nblk2, int cap2,
+                                                     int32_t *__restrict__ first)
+{
+    __shared__ int wsum[16];
+    __shared__ int rec_b[8], rec_num[8], rec_den[8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ntiles = meta[0];
+    int part = 0;
+    for (int b = tid; b < ntiles; b += 1024)
+        part += split_tile_cost(sorted_ids, b, P);
+    for (int m = 32; m; m >>= 1)
+        part += __shfl_xor(part, m, 64);
+    if (lane == 0)
+        wsum[wave] = part;
+    __syncthreads();
+    long long C = 0;
+    for (int w = 0; w < 16; ++w)
+        C += wsum[w];
+    __syncthreads();
+    // boundary x lies in the tile b with 8*S_b < x*C <= 8*(S_b + cost_b),
+    // S_b = cost of the tiles before b (each x has exactly one such tile)
+    long long carry = 0;
+    for (int base = 0; base < ntiles; base += 1024) {
+        const int b = base + tid;
+        const int c = b < ntiles ? split_tile_cost(sorted_ids, b, P) : 0;
+        int incl = c;
+        for (int m = 1; m < 64; m <<= 1) {
+            const int v = __shfl_up(incl, m, 64);
+            if (lane >= m)
+                incl += v;
+        }
+        if (lane == 63)
+            wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, chunk = 0;
+        for (int w = 0; w < 16; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            chunk += wsum[w];
+        }
+        const long long S = carry + before + incl - c;
+        if (b < ntiles)
+            for (int x = 1; x < 8; ++x) {
+                const long long t = (long long)x * C;
+                if (8 * S < t && t <= 8 * (S + c)) {
+                    rec_b[x] = b;
+                    rec_num[x] = (int)(t - 8 * S);
+                    rec_den[x] = 8 * c;
+                }
+            }
+        carry += chunk;
+        __syncthreads();
+    }
+    if (tid < 2) {
+        const int nblk = tid == 0 ? nblk13 : nblk2, cap = tid == 0 ? cap13 : cap2;
+        int B[9];
+        B[0] = 0;
+        B[8] = ntiles * nblk;
+        for (int x = 1; x < 8; ++x)   // the tile's items up to the cost target
+            B[x] = ntiles == 0 ? 0
+                               : rec_b[x] * nblk + (nblk * rec_num[x] + rec_den[x] - 1) / rec_den[x];
+        for (int x = 1; x < 8; ++x)
+            B[x] = min(B[x], B[x - 1] + cap);
+        for (int x = 7; x >= 1; --x)
+            B[x] = max(B[x], B[x + 1] - cap);
+        for (int x = 0; x < 9; ++x)
+            first[tid * kSplitEntries + x] = B[x];
+    }
+}
+
+hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream)
+{
+    if (d.block_m != Tile<2, 128, true>::BM)
+        return hipErrorInvalidValue;
+    const int o13 = Tile<2, 128, true>::OUTC, o2 = Tile<2, 128, false>::OUTC;
+    hipLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, stream, ws.sorted_ids, ws.meta,
+                       d.T * d.topk, (d.I + o13 - 1) / o13, tile_xcd_cap(d.max_tiles, d.I, true),
+                       (d.H + o2 - 1) / o2, tile_xcd_cap(d.max_tiles, d.H, false), ws.xcd_first);
+    return hipGetLastError();
+}
+
 // Load units in flight per wave of the decode-shaped kernel: as many as fit
 // without spilling.
 template <int BITS, int GS, bool W13>
@@ -1820,8 +1933,9 @@ static hipError_t gemm_dispatch(const GemmArgs &a, int variant, int max_tiles, h
         if (a.prepared)   // the tile kernel reads the checkpoint layout only
             return hipErrorNotSupported;
         using K_ = Tile<BITS, GS, W13>;
-        const long items = (long)max_tiles * ((a.N + K_::OUTC - 1) / K_::OUTC);
-        const long grid = (items + K_::kXcds - 1) / K_::kXcds * K_::kXcds;
+        if (!a.xcd_first)
+            return hipErrorInvalidValue;
+        const long grid = (long)K_::kXcds * tile_xcd_cap(max_tiles, a.N, W13);
         hipExtLaunchKernelGGL((tile_kernel<BITS, GS, W13>), dim3((unsigned)grid),
                               dim3(K_::NTHREADS), 0, stream, ev.start, ev.stop, 0, a);
     }
@@ -1867,6 +1981,7 @@ static GemmArgs w13_args(const int32_t *w13, const uint16_t *s13, const LayerDim
     a.clamp = d.clamp;
     a.tile_done = ws.tile_done;
     a.prepared = d.prepared;
+    a.xcd_first = ws.xcd_first;
     return a;
 }
 
@@ -1898,6 +2013,7 @@ static GemmArgs w2_args(const int32_t *w2, const uint16_t *s2, const float *topk
     a.topk = d.topk;
     a.tile_done = ws.tile_done;
     a.prepared = d.prepared;
+    a.xcd_first = ws.xcd_first + kSplitEntries;
     return a;
 }
 

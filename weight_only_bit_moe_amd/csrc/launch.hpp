@@ -23,7 +23,11 @@ struct Workspace {
     int32_t *chunk_counts;    // [align chunks][E + 1]: per-chunk expert counts, then invalid ids
     int32_t *done;            // [H / 64][16]: decode w2 workgroups finished per column block
     int32_t *tile_done;       // [max_tiles][16]: fused decode, w13 workgroups finished per tile
+    int32_t *xcd_first;       // [2][kSplitEntries]: tile kernel item range per XCD, w13 then w2
 };
+
+// Entries per GEMM of the tile kernel's XCD split: 8 range starts and the total.
+constexpr int kSplitEntries = 9;
 
 // Pairs per workgroup of the expert sort.
 // Pairs per sort workgroup: a multiple of 1024 (one placement step), the
@@ -61,6 +65,9 @@ struct LayerDims {
 // Expert-sorted tiles + activation reorder/bias + zeroed accumulator.
 hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerDims &d,
                         const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
+// Tile-kernel plans (block_m 64): split each GEMM's items over the XCDs by
+// cost, after the route launch (writes ws.xcd_first).
+hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream);
 // Fused gate/up WNA16 GEMM with the SwiGLU epilogue.
 hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
                       const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
