@@ -356,3 +356,36 @@ def test_full_workload_sampled_tokens(dev, cfg):
     rows = SAMPLES[cfg]
     ref = O.forward_layer(L, tokens=rows)
     G.assert_parity(y[rows], ref, f"config {cfg}")
+
+
+def test_tile_split_ranges_capped_at_launch_slots(dev):
+    """Prefill-shaped plan whose cost-balanced XCD split needs the cap: 108
+    full 64-row tiles of expert 0 followed by 27 one-row experts.  With one
+    column block per GEMM each XCD gets 26 workgroup slots, and the balanced
+    split would give the last XCD the 27 one-row tiles.  The capped ranges must
+    still cover every item once (checked through the output), and the table
+    the split kernel leaves in the workspace (ints 8..25: w13 then w2, 8 range
+    starts and the total each) must respect the cap."""
+    nfull, nsmall = 108, 27
+    T = 64 * nfull + nsmall
+    sp = spec(T=T, H=512, I=256, E=nsmall + 1, topk=1, **ACT)
+    L = make_layer(sp, seed=31)
+    ids = np.zeros((T, 1), np.int32)
+    ids[64 * nfull:, 0] = np.arange(1, nsmall + 1)
+    L.topk_ids = ids
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                            (sp.bits2, sp.group2))
+    assert plan["w13_variant"] == PRE and plan["block_m"] == 64
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    _, got = G.run_layer(L, dev, workspace=ws)
+    G.assert_parity(got, O.forward_layer(L), "capped XCD split")
+    table = ws[:128].view(torch.int32)[8:26].cpu().numpy().reshape(2, 9)
+    ntiles = nfull + nsmall
+    max_tiles = plan["max_tiles"]
+    per = (max_tiles + 7) // 8
+    cap = per + per // 2 + 1          # slots per XCD with one column block
+    for first in table:
+        lens = np.diff(first)
+        assert first[0] == 0 and first[8] == ntiles, first
+        assert np.all(lens >= 0) and np.all(lens <= cap), (first, cap)
+        assert lens.max() == cap, (first, cap)   # the cap did bind
