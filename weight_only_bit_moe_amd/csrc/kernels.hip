@@ -1816,8 +1816,18 @@ __global__ __launch_bounds__(1024) void split_kernel(const int32_t *__restrict__
     __shared__ int rec_b[8], rec_num[8], rec_den[8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ntiles = meta[0];
+    // the costs of this thread's first kCached tiles stay in registers for
+    // the second pass
+    constexpr int kCached = 4;
+    int cost[kCached];
     int part = 0;
-    for (int b = tid; b < ntiles; b += 1024)
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) {
+        const int b = tid + 1024 * i;
+        cost[i] = b < ntiles ? split_tile_cost(sorted_ids, b, P) : 0;
+        part += cost[i];
+    }
+    for (int b = tid + 1024 * kCached; b < ntiles; b += 1024)
         part += split_tile_cost(sorted_ids, b, P);
     for (int m = 32; m; m >>= 1)
         part += __shfl_xor(part, m, 64);
@@ -1831,9 +1841,14 @@ __global__ __launch_bounds__(1024) void split_kernel(const int32_t *__restrict__
     // boundary x lies in the tile b with 8*S_b < x*C <= 8*(S_b + cost_b),
     // S_b = cost of the tiles before b (each x has exactly one such tile)
     long long carry = 0;
-    for (int base = 0; base < ntiles; base += 1024) {
+    for (int base = 0, i = 0; base < ntiles; base += 1024, ++i) {
         const int b = base + tid;
-        const int c = b < ntiles ? split_tile_cost(sorted_ids, b, P) : 0;
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < kCached; ++j)
+            c = i == j ? cost[j] : c;
+        if (i >= kCached)
+            c = b < ntiles ? split_tile_cost(sorted_ids, b, P) : 0;
         int incl = c;
         for (int m = 1; m < 64; m <<= 1) {
             const int v = __shfl_up(incl, m, 64);
