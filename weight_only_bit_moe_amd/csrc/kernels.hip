@@ -603,7 +603,8 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float bet
 // Workgroup ids are spread over the 8 XCDs round-robin by the hardware; the
 // kernel gives each XCD a contiguous run of (tile, column block) items,
 // tile-major, so one XCD's L2 serves both the column blocks of a tile
-// (activation reuse) and consecutive tiles of one expert (weight reuse).
+// (activation reuse) and consecutive tiles of one expert (weight reuse).  The
+// runs are cut by estimated cost, not by count (split_kernel).
 // ---------------------------------------------------------------------------
 // LDS address (byte offset in the workgroup's LDS) of a __shared__ pointer.
 __device__ __forceinline__ uint32_t lds_address(const void *p)
