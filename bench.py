@@ -8,9 +8,11 @@ distributions (the expert weights stay the same), so consecutive steps touch
 mostly different experts and the weight stream comes from HBM rather than
 from the 256 MB last-level cache.
 
-The default workload is the decode-sized W2A16 layer (T=4, hidden 4096,
-intermediate 2048, 256 experts, top-6, 2-bit codes, group 128), which is
-HBM-bound; `--config 3/4/5` selects the other workloads.
+The default workload is the largest one, the large prefill (T=8192, hidden
+4096, intermediate 2048, 256 experts, top-8, w13 4-bit group 128, w2 2-bit
+group 64, Zipf routing), which is MFMA-bound; the same line carries, under
+"decode", the decode-sized W2A16 layer (T=4, top-6, 2-bit group 128), which
+is HBM-bound.  `--config 2/3/4` selects another workload as the headline.
 
 Decode-shaped workloads run on codes in the prepared order by default: the
 one-time moe_wna16_prepare reorder runs before warmup, outside the timed
@@ -22,8 +24,12 @@ Prints ONE JSON line.  `value` and `ms_per_step` come from K steps through the
 plain entry point (no events).  The same K steps are then run again with
 per-launch events (moe_wna16_forward_profiled, or the prepared entry with its
 event array), whose kernel dispatches carry their own start/stop events;
-`roofline` is for the kernel with the longest average duration in that pass.
-`cpu_baseline` is the CPU oracle on a bounded sample of the same workload.
+`roofline` is for the kernel with the longest average duration in that pass,
+and the per-step and per-launch p10/p50/p90 come from that pass.
+`algorithmic_bytes` counts the packed codes and scales of the experts routed
+to plus x and out; `implementation_bytes` lists this implementation's other
+traffic (act round trip, FP32 sum).  `cpu_baseline` is the CPU oracle on a
+bounded sample of the same workload.
 
 `--quantize` measures the quantizer instead and prints its own line.
 """
@@ -53,7 +59,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-decode-extra", dest="decode_extra", action="store_false",
+                    help="do not add the decode workload's figures to a prefill line")
     ap.add_argument("--batches", type=int, default=64,
                     help="distinct routing batches cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -150,23 +158,51 @@ def main():
         bench_quantize(args)
         return
 
-    import numpy as np
-    import torch
-
     import weight_only_bit_moe_amd as M
-    from weight_only_bit_moe_amd.inputs import CONFIGS, make_batch, make_config
-
     if not os.path.exists(M.LIB_PATH):
         from weight_only_bit_moe_amd import build as hip_build
         hip_build.build()
 
     cfg = args.config
+    result, L = measure_layer(cfg, args, args.steps, args.warmup, args.codes)
+    if args.decode_extra and cfg not in (2, 3):
+        # the decode half of the metric (HBM-bound, 4 tokens) on the same GPU,
+        # with its own step counts: a ~40 us step needs a few hundred untimed
+        # calls before the host's enqueue path and the clocks are steady
+        dec, _ = measure_layer(2, args, None, None, "auto")
+        result["decode"] = {k: dec[k] for k in (
+            "value", "unit", "ms_per_step", "steps", "warmup", "config", "roofline", "kernel_ms",
+            "step_ms_percentiles", "layer_hbm_gbs", "layer_hbm_frac", "experts_touched_per_step",
+            "algorithmic_bytes")}
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def percentiles(v):
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def measure_layer(cfg, args, steps, warmup, codes):
+    """Time `steps` layer calls on workload `cfg` after `warmup` untimed ones.
+    Returns (the JSON dict of the measurement, the host layer)."""
+    import numpy as np
+    import torch
+
+    import weight_only_bit_moe_amd as M
+    from weight_only_bit_moe_amd.inputs import make_batch, make_config
+
     decode = cfg in (2, 3)
     # Decode steps are ~40 us: a few hundred untimed calls bring the host's
     # enqueue path and the clocks to steady state (after 20 the launches of
     # one step were still ~3 us apart).
-    steps = args.steps if args.steps is not None else (1000 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (500 if decode else 10)
+    steps = steps if steps is not None else (1000 if decode else 20)
+    warmup = warmup if warmup is not None else (500 if decode else 10)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -177,16 +213,16 @@ def main():
     q13, q2 = (sp.bits13, sp.group13), (sp.bits2, sp.group2)
     plan = M.moe_wna16_plan(T, H, I, E, k, q13, q2)
     decode_shaped = plan["w13_variant"] == 2 and plan["w2_variant"] == 2
-    if args.codes == "prepared" and not decode_shaped:
+    if codes == "prepared" and not decode_shaped:
         print("--codes prepared needs a decode-shaped workload (--config 2 or 3)",
               file=sys.stderr)
         sys.exit(2)
-    args.prepared = args.codes == "prepared" or (args.codes == "auto" and decode_shaped)
+    prepared = codes == "prepared" or (codes == "auto" and decode_shaped)
     w13 = torch.from_numpy(L.w13.view(np.int32)).to(dev)
     s13 = torch.from_numpy(L.s13).to(dev)
     w2 = torch.from_numpy(L.w2.view(np.int32)).to(dev)
     s2 = torch.from_numpy(L.s2).to(dev)
-    if args.prepared:   # one-time setup, outside the timed region
+    if prepared:   # one-time setup, outside the timed region
         w13 = M.prepare(w13, sp.bits13, sp.group13)
         w2 = M.prepare(w2, sp.bits2, sp.group2)
         torch.cuda.synchronize(dev)
@@ -202,15 +238,15 @@ def main():
     ws = M.workspace_for(T, H, I, E, k, dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    clamp = sp.clamp
     fixed = (w13.data_ptr(), s13.data_ptr(), w2.data_ptr(), s2.data_ptr())
     call_args = []
     for x, ids, w in batches:
         call_args.append((x.data_ptr(), ids.data_ptr(), w.data_ptr()) + fixed +
-                         (T, H, I, E, k, q13, q2, sp.alpha, sp.beta, clamp, out.data_ptr(),
+                         (T, H, I, E, k, q13, q2, sp.alpha, sp.beta, sp.clamp, out.data_ptr(),
                           ws.data_ptr(), ws.numel(), stream))
+
     def step_plain(i):
-        if args.prepared:
+        if prepared:
             st = M.moe_wna16_forward_prepared(*call_args[i % nb], None)
         else:
             st = M.moe_wna16_forward(*call_args[i % nb])
@@ -238,7 +274,7 @@ def main():
     # this pass is not the one whose wall time is reported)
     torch.cuda.synchronize(dev)
     t2 = time.perf_counter()
-    profiled = M.moe_wna16_forward_prepared if args.prepared else M.moe_wna16_forward_profiled
+    profiled = M.moe_wna16_forward_prepared if prepared else M.moe_wna16_forward_profiled
     for i in range(steps):
         st = profiled(*call_args[i % nb], events[i])
         if st != 0:
@@ -246,11 +282,15 @@ def main():
     torch.cuda.synchronize(dev)
     t3 = time.perf_counter()
     ms_events = (t3 - t2) * 1e3 / steps
+    meta = M.workspace_meta(ws, T, H, I, E, k).cpu().numpy()
+    if meta[2] != 0:
+        raise RuntimeError(f"{meta[2]} fused decode waits gave up: the output is unreliable")
 
     # one entry per launch: steps that share a launch (plan: gemms_one_launch,
-    # convert_in_w2) are timed as that launch
+    # convert_in_w2) are timed as that launch; with 64-row tiles the routing
+    # step also holds the split of the tile kernels' items over the XCDs
     one = bool(plan["gemms_one_launch"])
-    launches = [("route", 0, 1)]
+    launches = [("route" if decode_shaped else "route+split", 0, 1)]
     launches += [("w13+w2", 2, 5)] if one else [("w13", 2, 3), ("w2", 4, 5)]
     if not plan["convert_in_w2"]:
         launches.append(("convert", 6, 7))
@@ -263,8 +303,13 @@ def main():
             kern_ms[name].append(hip.elapsed_ms(ev[a0], ev[a1]))
         step_gpu_ms.append(hip.elapsed_ms(ev[0], ev[last_stop]))
     avg = {n: float(np.mean(v)) for n, v in kern_ms.items()}
+    for e in events:
+        for h in e:
+            hip.destroy(h)
 
-    # algorithmic work of each step (bookkeeping from the routing ids)
+    # algorithmic work of each step (bookkeeping from the routing ids):
+    # bytes = packed codes + scales of the distinct experts routed to + x
+    # (read by w13) + out (written after w2); flops = 2 P (2I H + H I)
     b13 = per_expert_bytes(sp.bits13, sp.group13, 2 * I, H)
     b2 = per_expert_bytes(sp.bits2, sp.group2, H, I)
     touched = []
@@ -272,15 +317,15 @@ def main():
         ids = host_batches[i % nb][0]
         touched.append(len(np.unique(ids[(ids >= 0) & (ids < E)])))
     mean_touched = float(np.mean(touched))
-    alg_bytes = {
-        "w13": mean_touched * b13 + T * H * 2 + P * I * 2,
-        "w2": mean_touched * b2 + P * I * 2 + T * H * 4,
-    }
+    alg_bytes = {"w13": mean_touched * b13 + T * H * 2, "w2": mean_touched * b2 + T * H * 2}
     alg_flops = {"w13": 2.0 * P * 2 * I * H, "w2": 2.0 * P * H * I}
     alg_bytes["w13+w2"] = alg_bytes["w13"] + alg_bytes["w2"]
     alg_flops["w13+w2"] = alg_flops["w13"] + alg_flops["w2"]
-    layer_bytes = mean_touched * (b13 + b2) + T * H * 2 * 2
-    layer_flops = alg_flops["w13"] + alg_flops["w2"]
+    layer_bytes = alg_bytes["w13+w2"]
+    layer_flops = alg_flops["w13+w2"]
+    # traffic of this implementation outside those bytes (not algorithmic):
+    # act written by w13 and read by w2, the FP32 sum (atomics, then rounding)
+    impl_bytes = {"act_write_read": 2.0 * P * I * 2, "fp32_sum": 3.0 * T * H * 4}
 
     dom = max((n for n in avg if n.startswith("w")), key=lambda n: avg[n])
     if decode:
@@ -295,8 +340,9 @@ def main():
     roof["kernel_ms"] = avg[dom]
     roof["algorithmic_bytes" if decode else "algorithmic_flops"] = (
         alg_bytes[dom] if decode else alg_flops[dom])
-    traffic_file = args.traffic_file or os.path.join(
-        ROOT, "profiles", f"counters_{sp.name}{'-prepared' if args.prepared else ''}.md")
+    traffic_file = args.traffic_file if cfg == args.config else None
+    traffic_file = traffic_file or os.path.join(
+        ROOT, "profiles", f"counters_{sp.name}{'-prepared' if prepared else ''}.md")
     roof["traffic"] = kernel_traffic(traffic_file, dom)
 
     value = T / (ms_per_step * 1e-3)
@@ -316,28 +362,29 @@ def main():
         "config": {"workload": sp.name, "T": T, "hidden": H, "intermediate": I, "experts": E,
                    "topk": k, "w13": f"W{sp.bits13} g{sp.group13}",
                    "w2": f"W{sp.bits2} g{sp.group2}", "block_m": plan["block_m"],
-                   "codes": "prepared order" if args.prepared else "checkpoint order",
+                   "codes": "prepared order" if prepared else "checkpoint order",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "kernel_ms": avg,
+        "kernel_ms_percentiles": {n: percentiles(v) for n, v in kern_ms.items()},
+        "step_ms_percentiles": percentiles(step_gpu_ms),
         "kernel_timing": "HIP events in each launch's dispatch packet, second pass of the "
-                         "same K steps (same kernels) on the same stream",
+                         "same K steps (same kernels) on the same stream; percentiles over "
+                         "the K steps of that pass",
         "ms_per_step_with_events": ms_events,
         "gpu_ms_per_step_events": float(np.mean(step_gpu_ms)),
+        "algorithmic_bytes": layer_bytes,
+        "algorithmic_flops": layer_flops,
+        "implementation_bytes": impl_bytes,
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
         "layer_hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_mfma_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "experts_touched_per_step": mean_touched,
     }
-
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
-    for e in events:
-        for h in e:
-            hip.destroy(h)
-    print(json.dumps(result), flush=True)
+    del batches, w13, w2, s13, s2, ws, out
+    torch.cuda.empty_cache()
+    return result, L
 
 
 # Lane operations per (weight, candidate) of the quantizer's definition: the
@@ -496,11 +543,13 @@ def cpu_baseline(L, budget_s):
 
     sp = L.spec
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    # sample: whole batches when the batch is small, else a slice of tokens
+    # sample: whole batches when the batch is small, else a slice of tokens;
+    # the probe holds enough pairs to keep every thread busy, like the sample
+    n0 = min(sp.T, -(-threads // sp.topk))
     t0 = time.perf_counter()
-    probe = oracle.forward_layer(L, tokens=[0], nthreads=threads)
-    per_token = time.perf_counter() - t0
-    ntok = int(max(1, min(sp.T, budget_s / max(per_token, 1e-6) * min(threads, sp.topk))))
+    probe = oracle.forward_layer(L, tokens=list(range(n0)), nthreads=threads)
+    per_token = (time.perf_counter() - t0) / n0
+    ntok = int(max(1, min(sp.T, budget_s / max(per_token, 1e-6))))
     tokens = list(range(ntok))
     done, elapsed, reps = 0, 0.0, 0
     while elapsed < budget_s or reps == 0:
@@ -514,8 +563,22 @@ def cpu_baseline(L, budget_s):
     used = min(threads, ntok * sp.topk)
     del probe
     return {"value": done / elapsed, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{ntok} of {sp.T} tokens x {reps} pass(es) of workload {sp.name}, "
                       f"{elapsed:.1f} s, float64"}
+
+
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 if __name__ == "__main__":

@@ -130,7 +130,9 @@ int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_
  * moe_wna16_forward with per-step timing; it launches the same kernels as
  * moe_wna16_forward.  `events` is a HOST array of 8 caller-created
  * hipEvent_t; for the four steps of the layer (in order: routing and
- * activation reorder, w13 + SwiGLU, w2 + scatter-add, BF16 rounding) step i
+ * activation reorder -- with the prefill-shaped plan also the split of the
+ * tile kernels' items over the XCDs, a launch of its own --, w13 + SwiGLU,
+ * w2 + scatter-add, BF16 rounding) step i
  * records events[2i] when its launch starts and events[2i+1] when it ends,
  * from the dispatch packets themselves (no extra packets on the stream).
  * Steps that share a launch (see moe_wna16_plan_t: gemms_one_launch,
@@ -151,7 +153,10 @@ int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const flo
 
 /*
  * Expert-sorted tile layout of the T*topk (token, slot) pairs, pair index
- * p = t*topk + j.  Bit-exact and deterministic:
+ * p = t*topk + j: the grouping of an indexed MoE's routed pairs by expert
+ * that the PR's BF16 "indexed MoE" path runs on ("What this branch adds"
+ * item 3), on its own.  The layout is this library's (the pages do not
+ * print one).  Bit-exact and deterministic:
  *   expert_offsets[E+1]  exclusive prefix sum of each expert's pair count
  *                        rounded up to a multiple of block_m
  *   sorted_ids[]         slot expert_offsets[e] + r holds the r-th smallest p
@@ -180,6 +185,49 @@ int moe_wna16_align(const int32_t *topk_ids, int T, int topk, int E, int block_m
  * Same size checks and status codes as moe_wna16_workspace_size.
  */
 int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t *offset_out);
+
+/*
+ * Where a moe_wna16_forward call with these sizes keeps, inside its
+ * workspace, the results of its own expert sort and its status words (byte
+ * offsets from the start of the workspace).  The contents are valid once the
+ * call has completed and are overwritten by the next call on the same
+ * workspace; they let a caller check the sort the layer actually ran (the
+ * expert-sorted tile layout the PR's BF16 "indexed MoE" path needs, "What
+ * this branch adds" item 3) and whether the call completed normally.
+ *
+ *   meta            int32 words:
+ *                   [0] num_tiles of the layer's sort (expert_offsets[E] / block_m)
+ *                   [1] ids outside [0, E)
+ *                   [2] fused decode waits that gave up: 0 after a normal call.  In
+ *                       the one-launch decode plan (moe_wna16_plan_t.gemms_one_launch)
+ *                       each down-projection workgroup waits, with a bounded spin, for
+ *                       the gate/up workgroups of its tile; a non-zero count means a
+ *                       wait ended at its bound and that call's output is unreliable
+ *                   [3..7] reserved, [8..25] the prefill tile kernels' split of their
+ *                       (tile, column block) items over the 8 XCDs (gate/up then down:
+ *                       8 range starts and the item count each)
+ *   expert_offsets  int32 [E + 1]     \
+ *   sorted_ids      int32 [num_tiles * block_m]   the tile layout of
+ *   tile_expert     int32 [num_tiles]             moe_wna16_align, with the
+ *   inv_perm        int32 [T * topk]  /           plan's block_m
+ *   out_f32         float [T, H]      the routed sum before its BF16 rounding
+ *   total           = moe_wna16_workspace_size
+ *
+ * *layout_out is a HOST pointer.  Same size checks and status codes as
+ * moe_wna16_workspace_size.
+ */
+typedef struct {
+    size_t meta;
+    size_t expert_offsets;
+    size_t sorted_ids;
+    size_t tile_expert;
+    size_t inv_perm;
+    size_t out_f32;
+    size_t total;
+} moe_wna16_workspace_layout_t;
+
+int moe_wna16_workspace_layout(int T, int H, int I, int E, int topk,
+                               moe_wna16_workspace_layout_t *layout_out);
 
 /*
  * Quantizer: float weights -> the packed codes and scales the layer reads

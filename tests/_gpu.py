@@ -38,11 +38,14 @@ def to_device(L, dev):
     )
 
 
-def run_layer(L, dev, d=None, out=None, workspace=None, prepared=False):
+def run_layer(L, dev, d=None, out=None, workspace=None, prepared=False, check_sort=True):
     """Run the layer; returns (BF16 output tensor, FP32 sum as float64 numpy).
-    Also checks that the output is the RNE rounding of the FP32 sum.  With
-    prepared=True the codes are first put in the prepared order on the GPU
-    and the prepared entry point runs."""
+    Also checks that the output is the RNE rounding of the FP32 sum, that no
+    fused decode wait gave up, and (check_sort) that the expert sort the
+    layer itself ran -- read back from its workspace -- equals the oracle's
+    bit for bit at the plan's tile size.  With prepared=True the codes are
+    first put in the prepared order on the GPU and the prepared entry point
+    runs."""
     sp = L.spec
     d = d or to_device(L, dev)
     clamp = None if math.isinf(sp.clamp) else sp.clamp
@@ -61,7 +64,33 @@ def run_layer(L, dev, d=None, out=None, workspace=None, prepared=False):
     f32 = M.workspace_f32_sum(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
     bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(bits, f32_to_bf16_bits(f32)), "BF16 output is not RNE(FP32 sum)"
+    meta = M.workspace_meta(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
+    assert meta[2] == 0, f"{meta[2]} fused decode waits gave up"
+    if check_sort:
+        assert_layer_sort(L, workspace)
     return y, f32.astype(np.float64)
+
+
+def layer_sort(L, workspace):
+    """The expert sort a completed forward on layer L ran (plan's block_m)."""
+    sp = L.spec
+    bm = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                          (sp.bits2, sp.group2))["block_m"]
+    return bm, M.workspace_sort(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk, bm)
+
+
+def assert_align_equal(got, ref):
+    assert got["num_tiles"] == ref["num_tiles"], (got["num_tiles"], ref["num_tiles"])
+    assert got["bad_ids"] == ref["bad_ids"], (got["bad_ids"], ref["bad_ids"])
+    for k in ("sorted_ids", "tile_expert", "expert_offsets", "inv_perm"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def assert_layer_sort(L, workspace):
+    """The layer's own sort equals the oracle's, bit for bit."""
+    from oracle import oracle as O
+    bm, got = layer_sort(L, workspace)
+    assert_align_equal(got, O.align(L.topk_ids, L.spec.E, bm))
 
 
 def to_f64(y):

@@ -210,3 +210,25 @@ def test_forward_prepared_checks_like_forward(lib):
     zero = list(args)
     zero[7] = 0
     assert f(*zero) == Bd.OK
+
+
+def test_workspace_layout_consistent(lib):
+    """The layout query agrees with the size and FP32-offset queries, and its
+    pieces are 256-byte aligned, in bounds and large enough for their arrays."""
+    for T, H, I, E, k in [(4, 4096, 2048, 256, 6), (8192, 4096, 2048, 256, 8), (0, 256, 128, 8, 2),
+                          (7169, 128, 128, 256, 1)]:
+        lay = M.moe_wna16_workspace_layout(T, H, I, E, k)
+        assert lay["total"] == M.moe_wna16_workspace_size(T, H, I, E, k)
+        assert lay["out_f32"] == M.moe_wna16_workspace_f32_offset(T, H, I, E, k)
+        P = T * k
+        need = {"meta": 26 * 4, "expert_offsets": (E + 1) * 4, "inv_perm": P * 4,
+                "sorted_ids": (P // 4 + min(E, P)) * 4 * 4, "tile_expert": (P // 4 + min(E, P)) * 4,
+                "out_f32": T * H * 4}
+        spans = sorted((lay[n], lay[n] + need[n]) for n in need)
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+            assert a1 <= b0, (T, spans)
+        assert spans[-1][1] <= lay["total"]
+        assert all(lay[n] % 256 == 0 for n in need)
+    with pytest.raises(M.MoeWna16Error):
+        M.moe_wna16_workspace_layout(4, 100, 2048, 256, 6)
+    assert lib.moe_wna16_workspace_layout(4, 4096, 2048, 256, 6, None) == Bd.EINVAL

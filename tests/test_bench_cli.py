@@ -39,3 +39,15 @@ def test_traffic_only_from_a_summary_of_the_current_source(tmp_path):
     stale.write_text("kernel_source_sha256: " + "0" * 64 + "\n\ntraffic_bytes_per_launch[w13+w2]: 1.5e+08\n")
     assert bench.kernel_traffic(str(stale), "w13+w2", str(src)) is None
     assert bench.kernel_traffic(str(tmp_path / "missing.md"), "w13+w2", str(src)) is None
+
+
+def test_percentiles_and_cpu_model():
+    p = bench.percentiles(list(range(101)))
+    assert (p["p10"], p["p50"], p["p90"]) == (10.0, 50.0, 90.0)
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_algorithmic_bytes_per_expert():
+    # 2-bit g128 gate/up of one expert at H=4096, I=2048: 4 MiB codes + 256 KiB scales
+    assert bench.per_expert_bytes(2, 128, 4096, 4096) == 4 * 2 ** 20 + 256 * 2 ** 10
+    assert bench.per_expert_bytes(2, 64, 4096, 2048) == 2 * 2 ** 20 + 256 * 2 ** 10

@@ -45,11 +45,7 @@ def gpu_align(ids_np, E, bm, dev):
                 bad_ids=int(r["bad_ids"][0]))
 
 
-def assert_align_equal(got, ref):
-    assert got["num_tiles"] == ref["num_tiles"]
-    assert got["bad_ids"] == ref["bad_ids"]
-    for k in ("sorted_ids", "tile_expert", "expert_offsets", "inv_perm"):
-        assert np.array_equal(got[k], ref[k]), k
+assert_align_equal = G.assert_align_equal
 
 
 def _align_cases():
@@ -343,19 +339,96 @@ def test_reused_workspace_and_output(dev):
 # full-size workloads, sampled tokens
 # --------------------------------------------------------------------------
 
-SAMPLES = {2: [0, 1, 2, 3], 3: [0, 17, 40, 63], 4: [0, 511, 1024, 2047], 5: [0, 3000, 8191]}
+def sampled_tokens(L, ws, n=64):
+    """Tokens of a full-size prefill-shaped layer worth checking one by one:
+    those in the tiles on both sides of every XCD range boundary of both
+    GEMMs (read from the split table the layer left in its workspace), the
+    first and last tile, tokens routed to the 8 least-used experts, then
+    evenly spaced tokens up to n."""
+    sp = L.spec
+    T, k = sp.T, sp.topk
+    bm, srt = G.layer_sort(L, ws)
+    meta = M.workspace_meta(ws, T, sp.H, sp.I, sp.E, k).cpu().numpy()
+    ntiles = srt["num_tiles"]
+    picked = []
+
+    def add_tile(b):
+        if 0 <= b < ntiles:
+            rows = srt["sorted_ids"][b * bm:(b + 1) * bm]
+            real = rows[rows < T * k]
+            picked.extend([int(real[0]) // k, int(real[-1]) // k])
+
+    if bm == 64:
+        for g, outc, N in ((0, 256, sp.I), (1, 512, sp.H)):   # items per tile: column blocks
+            nblk = -(-N // outc)
+            first = meta[8 + 9 * g: 17 + 9 * g]
+            for x in range(1, 8):
+                add_tile(int(first[x]) // nblk)
+                add_tile((int(first[x]) - 1) // nblk)
+    add_tile(0)
+    add_tile(ntiles - 1)
+    ids = L.topk_ids
+    counts = np.bincount(ids[(ids >= 0) & (ids < sp.E)].ravel(), minlength=sp.E)
+    for e in np.argsort(np.where(counts > 0, counts, 1 << 30), kind="stable")[:8]:
+        if counts[e]:
+            picked.append(int(np.argwhere(ids == e)[0][0]))
+    out = list(dict.fromkeys(picked))[:n]
+    for t in np.linspace(0, T - 1, n).astype(int):
+        if len(out) >= n:
+            break
+        if t not in out:
+            out.append(int(t))
+    return sorted(out)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_workload_sampled_tokens(dev, cfg):
+    """The workloads at full size, in the launch configuration bench.py times:
+    every token of the decode workloads, and 64 tokens of each prefill
+    workload chosen at the XCD range boundaries, the first and last tile and
+    the least-used experts.  The layer's own sort is checked bit for bit
+    (run_layer)."""
     L = make_config(cfg)
     sp = L.spec
     print(f"config {cfg} {sp.name}: T={sp.T} E={sp.E} k={sp.topk}", flush=True)
-    _, y = G.run_layer(L, dev)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    _, y = G.run_layer(L, dev, workspace=ws)
     assert np.all(np.isfinite(y))
-    rows = SAMPLES[cfg]
+    rows = list(range(sp.T)) if sp.T <= 64 else sampled_tokens(L, ws)
+    assert len(rows) == min(sp.T, 64)
     ref = O.forward_layer(L, tokens=rows)
     G.assert_parity(y[rows], ref, f"config {cfg}")
+
+
+@pytest.mark.parametrize("T,k,routing,bad", [(896, 8, "zipf", False), (7169, 1, "uniform", True),
+                                             (2048, 4, "zipf", False), (2048, 6, "zipf", True),
+                                             (8192, 8, "zipf", True)])
+def test_layer_sort_bit_exact_across_sort_paths(dev, T, k, routing, bad):
+    """The layer's own expert sort on both sides of the route kernel's switch
+    from recounting every pair (up to 7 sort workgroups: P = 7168) to summing
+    per-chunk counts from the count launch (8 and more: P = 7169, 8192,
+    12288, 65536), 64-row tiles, 256 experts: sorted ids, tile experts,
+    offsets, inverse permutation and tile count equal the oracle's bit for
+    bit (run_layer), with invalid ids counted in some cases, and the layer
+    output within tolerance."""
+    P = T * k
+    sp = spec(T=T, H=128, I=128, E=256, topk=k, routing=routing, bits13=2, bits2=2, **ACT)
+    L = make_layer(sp, seed=P)
+    if bad:
+        flat = L.topk_ids.reshape(-1).copy()
+        where = np.random.default_rng(P).choice(P, size=15, replace=False)
+        flat[where] = np.repeat([-1, 256, 1 << 20], 5)
+        L.topk_ids = flat.reshape(T, k)
+    plan = M.moe_wna16_plan(T, 128, 128, 256, k, (2, 128), (2, 128))
+    assert plan["block_m"] == 64
+    # sort workgroups: chunks of a multiple of 1024 pairs, at most 16 of them
+    per = math.ceil(P / 16)
+    chunk = max(1024, math.ceil(per / 1024) * 1024)
+    assert (math.ceil(P / chunk) >= 8) == (P >= 7169)
+    ws = M.workspace_for(T, 128, 128, 256, k, dev)
+    _, got = G.run_layer(L, dev, workspace=ws)
+    assert G.layer_sort(L, ws)[1]["bad_ids"] == (15 if bad else 0)
+    G.assert_parity(got, O.forward_layer(L), f"P={P}")
 
 
 def test_tile_split_ranges_capped_at_launch_slots(dev):

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_wna16.so")
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP = 0, -1, -2, -3, -4, -5, -6
 
 #: every symbol include/moe_wna16.h declares
-EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset", "moe_wna16_plan",
+EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset",
+            "moe_wna16_workspace_layout", "moe_wna16_plan",
             "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_align",
             "moe_wna16_quantize", "moe_wna16_prepare", "moe_wna16_forward_prepared",
             "moe_wna16_status_string")
@@ -32,6 +33,11 @@ class Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
                 ("w13_variant", ctypes.c_int32), ("w2_variant", ctypes.c_int32),
                 ("gemms_one_launch", ctypes.c_int32), ("convert_in_w2", ctypes.c_int32)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("meta", "expert_offsets", "sorted_ids",
+                                                "tile_expert", "inv_perm", "out_f32", "total")]
 
 
 class MoeWna16Error(RuntimeError):
@@ -59,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_wna16_workspace_size.restype = i
     lib.moe_wna16_workspace_f32_offset.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
     lib.moe_wna16_workspace_f32_offset.restype = i
+    lib.moe_wna16_workspace_layout.argtypes = [i, i, i, i, i, ctypes.POINTER(WorkspaceLayout)]
+    lib.moe_wna16_workspace_layout.restype = i
     lib.moe_wna16_plan.argtypes = [i, i, i, i, i, QParams, QParams, ctypes.POINTER(Plan)]
     lib.moe_wna16_plan.restype = i
     lib.moe_wna16_forward.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, QParams, QParams,
@@ -100,6 +108,43 @@ def moe_wna16_workspace_f32_offset(T: int, H: int, I: int, E: int, topk: int) ->
     if st != OK:
         raise MoeWna16Error(st, "moe_wna16_workspace_f32_offset")
     return out.value
+
+
+def moe_wna16_workspace_layout(T: int, H: int, I: int, E: int, topk: int) -> dict:
+    """Byte offsets of the sort results, status words and FP32 sum inside a
+    forward's workspace (dict with the struct's field names)."""
+    lay = WorkspaceLayout()
+    st = load_library().moe_wna16_workspace_layout(T, H, I, E, topk, ctypes.byref(lay))
+    if st != OK:
+        raise MoeWna16Error(st, "moe_wna16_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in WorkspaceLayout._fields_}
+
+
+def workspace_meta(workspace, T, H, I, E, topk):
+    """The 26 int32 status words of a completed forward (see the header):
+    [0] tiles, [1] ids outside [0, E), [2] fused decode waits that gave up,
+    [8..25] the prefill tile kernels' XCD split."""
+    torch = _torch()
+    off = moe_wna16_workspace_layout(T, H, I, E, topk)["meta"]
+    return workspace[off: off + 26 * 4].view(torch.int32)
+
+
+def workspace_sort(workspace, T, H, I, E, topk, block_m):
+    """The expert sort a completed forward ran, read from its workspace: a dict
+    like align() returns, cut to the tile count (host numpy arrays)."""
+    torch = _torch()
+    lay = moe_wna16_workspace_layout(T, H, I, E, topk)
+    meta = workspace_meta(workspace, T, H, I, E, topk).cpu().numpy()
+    n = int(meta[0])
+    P = T * topk
+
+    def ints(name, count):
+        off = lay[name]
+        return workspace[off: off + count * 4].view(torch.int32).cpu().numpy()
+
+    return dict(sorted_ids=ints("sorted_ids", n * block_m), tile_expert=ints("tile_expert", n),
+                expert_offsets=ints("expert_offsets", E + 1), inv_perm=ints("inv_perm", P),
+                num_tiles=n, bad_ids=int(meta[1]))
 
 
 def workspace_f32_sum(workspace, T, H, I, E, topk):

@@ -183,6 +183,25 @@ int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t 
     return MOE_WNA16_OK;
 }
 
+int moe_wna16_workspace_layout(int T, int H, int I, int E, int topk,
+                               moe_wna16_workspace_layout_t *layout_out)
+{
+    if (!layout_out)
+        return MOE_WNA16_EINVAL;
+    const int st = check_sizes(T, H, I, E, topk);
+    if (st != MOE_WNA16_OK)
+        return st;
+    const Layout L = layout_of(T, H, I, E, topk);
+    layout_out->meta = L.meta;
+    layout_out->expert_offsets = L.offsets;
+    layout_out->sorted_ids = L.sorted;
+    layout_out->tile_expert = L.tiles;
+    layout_out->inv_perm = L.inv;
+    layout_out->out_f32 = L.outf32;
+    layout_out->total = L.total;
+    return MOE_WNA16_OK;
+}
+
 int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
                    moe_wna16_qparams q2, moe_wna16_plan_t *plan_out)
 {
@@ -275,11 +294,15 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
         for (int i = 0; i < 4; ++i)
             ev[i] = wna16::KernelEvents{events[2 * i], events[2 * i + 1]};
     const uint16_t *xb = static_cast<const uint16_t *>(x);
-    if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, ev[0]))) !=
+    // Tile-kernel plans split the items over the XCDs right after the sort:
+    // the split launch belongs to the routing step and carries its stop event.
+    const bool split = plan.w13_variant == 1 || plan.w2_variant == 1;
+    const wna16::KernelEvents route_ev{ev[0].start, split ? nullptr : ev[0].stop};
+    if ((st = hip_status(wna16::launch_route(xb, topk_ids, d, ws, stream, route_ev))) !=
         MOE_WNA16_OK)
         return st;
-    if ((plan.w13_variant == 1 || plan.w2_variant == 1) &&
-        (st = hip_status(wna16::launch_split(d, ws, stream))) != MOE_WNA16_OK)
+    if (split && (st = hip_status(wna16::launch_split(
+                      d, ws, stream, wna16::KernelEvents{nullptr, ev[0].stop}))) != MOE_WNA16_OK)
         return st;
     // Small outputs: the last decode w2 workgroup of each column block rounds
     // that block to BF16, which saves the convert launch.  Decode shapes whose

@@ -437,6 +437,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         ws.done[i] = 0;
     for (size_t i = first; i < (size_t)tdone_n; i += nzero_threads)
         ws.tile_done[i] = 0;
+    if (first == 0)
+        ws.meta[2] = 0;   // fused decode waits that gave up (counted by this call)
 }
 
 // ---------------------------------------------------------------------------
@@ -464,6 +466,7 @@ struct GemmArgs {
     int32_t *done;            // W2 decode: finished workgroups per column block, 16 ints apart
     int32_t *tile_done;       // fused decode: w13 workgroups finished per tile, 16 ints apart
     int tile_target;          // fused decode w2: w13 workgroups per tile
+    int32_t *status;          // fused decode w2: count of waits that gave up (meta word 2)
     int K;                    // reduction length (H for w13, I for w2)
     int N;                    // output columns (I gate columns for w13, H for w2)
     int P, topk;
@@ -1444,12 +1447,18 @@ struct Stream {
             // items: wait (bounded) until all of them are done
             if (tid == 0) {
                 const int32_t *cnt = args.tile_done + b * 16;
-                for (int it = 0; it < (1 << 22); ++it) {
-                    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                        args.tile_target)
-                        break;
-                    __builtin_amdgcn_s_sleep(2);
+                bool ready = false;
+                for (int it = 0; it < (1 << 22) && !ready; ++it) {
+                    ready = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                            args.tile_target;
+                    if (!ready)
+                        __builtin_amdgcn_s_sleep(2);
                 }
+                // a wait that reached its bound is counted where the host can
+                // read it: the act rows staged below may then be incomplete
+                if (!ready)
+                    __hip_atomic_fetch_add(args.status, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
         }
@@ -1894,14 +1903,16 @@ __global__ __launch_bounds__(1024) void split_kernel(const int32_t *__restrict__
     }
 }
 
-hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream)
+hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream,
+                        const KernelEvents &ev)
 {
     if (d.block_m != Tile<2, 128, true>::BM)
         return hipErrorInvalidValue;
     const int o13 = Tile<2, 128, true>::OUTC, o2 = Tile<2, 128, false>::OUTC;
-    hipLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, stream, ws.sorted_ids, ws.meta,
-                       d.T * d.topk, (d.I + o13 - 1) / o13, tile_xcd_cap(d.max_tiles, d.I, true),
-                       (d.H + o2 - 1) / o2, tile_xcd_cap(d.max_tiles, d.H, false), ws.xcd_first);
+    hipExtLaunchKernelGGL(split_kernel, dim3(1), dim3(1024), 0, stream, ev.start, ev.stop, 0,
+                          ws.sorted_ids, ws.meta, d.T * d.topk, (d.I + o13 - 1) / o13,
+                          tile_xcd_cap(d.max_tiles, d.I, true), (d.H + o2 - 1) / o2,
+                          tile_xcd_cap(d.max_tiles, d.H, false), ws.xcd_first);
     return hipGetLastError();
 }
 
@@ -2028,6 +2039,7 @@ static GemmArgs w2_args(const int32_t *w2, const uint16_t *s2, const float *topk
     a.P = d.T * d.topk;
     a.topk = d.topk;
     a.tile_done = ws.tile_done;
+    a.status = ws.meta + 2;
     a.prepared = d.prepared;
     a.xcd_first = ws.xcd_first + kSplitEntries;
     return a;

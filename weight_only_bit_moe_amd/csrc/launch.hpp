@@ -10,7 +10,7 @@ namespace wna16 {
 
 // Device workspace regions of one forward call.
 struct Workspace {
-    int32_t *meta;            // [0] num_tiles, [1] bad ids
+    int32_t *meta;            // [0] num_tiles, [1] bad ids, [2] fused decode waits that gave up
     int32_t *expert_offsets;  // [E + 1]
     int32_t *sorted_ids;      // [max_slots]
     int32_t *tile_expert;     // [max_tiles]
@@ -67,7 +67,8 @@ hipError_t launch_route(const uint16_t *x, const int32_t *topk_ids, const LayerD
                         const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
 // Tile-kernel plans (block_m 64): split each GEMM's items over the XCDs by
 // cost, after the route launch (writes ws.xcd_first).
-hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream);
+hipError_t launch_split(const LayerDims &d, const Workspace &ws, hipStream_t stream,
+                        const KernelEvents &ev);
 // Fused gate/up WNA16 GEMM with the SwiGLU epilogue.
 hipError_t launch_w13(const int32_t *w13, const uint16_t *s13, const LayerDims &d,
                       const Workspace &ws, hipStream_t stream, const KernelEvents &ev);
