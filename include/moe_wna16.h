@@ -62,7 +62,9 @@ typedef enum {
     MOE_WNA16_EALIGN = -3,      /* pointer not aligned as required          */
     MOE_WNA16_EWORKSPACE = -4,  /* workspace smaller than workspace_size    */
     MOE_WNA16_EARCH = -5,       /* current device is not gfx950             */
-    MOE_WNA16_EHIP = -6         /* a HIP runtime call or launch failed      */
+    MOE_WNA16_EHIP = -6,        /* a HIP runtime call or launch failed      */
+    MOE_WNA16_ESCRATCH = -7     /* moe_wna16_forward_noalloc: the call needs */
+                                /* more than the library's 32 MiB scratch    */
 } moe_wna16_status;
 
 /* Quantization of one projection: bits in {2, 4}; group in {32, 64, 128}. */
@@ -303,6 +305,37 @@ int moe_wna16_forward_prepared(const void *x, const int32_t *topk_ids, const flo
                                moe_wna16_qparams q2, float alpha, float beta, float clamp,
                                void *out, void *workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t *events);
+
+/*
+ * moe_wna16_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace.  Instead it uses a scratch array inside
+ * the library: 32 MiB of device memory per GPU, held from the first call on
+ * that GPU until the process ends.  It allocates nothing itself (no hipMalloc,
+ * no allocating library call); its first call on a device looks the array's
+ * address up once.
+ *
+ * Same arguments (codes in the packed order), checks, status codes and result
+ * as moe_wna16_forward without its workspace arguments, except:
+ *   - The workspace this call needs, laid out for the plan's tile size
+ *     (moe_wna16_plan_t.block_m), must fit the 32 MiB; otherwise it returns
+ *     MOE_WNA16_ESCRATCH before any launch.  Every decode-shaped call
+ *     (block_m 4) with T <= 512 at H = 4096, I = 2048, E = 256 fits;
+ *     prefill-shaped calls at those sizes do not (their 64-row tiles pad
+ *     every expert's act rows) and need moe_wna16_forward.
+ *   - Every call on one GPU uses that GPU's one array.  Calls ordered on one
+ *     stream are fine (each clears what must start at zero); calls that
+ *     overlap on one GPU -- on different streams, or from several host
+ *     threads without ordering -- race on it and give undefined results.
+ *   - The array keeps the last call's contents; nothing in it is meant to be
+ *     read by the caller.
+ */
+int moe_wna16_forward_noalloc(const void *x, const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *w13_packed, const uint16_t *w13_scales,
+                              const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H,
+                              int I, int E, int topk, moe_wna16_qparams q13,
+                              moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                              void *out, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *moe_wna16_status_string(int status);

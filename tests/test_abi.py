@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert M.moe_wna16_status_string(st) not in ("", "unknown status")
     assert M.moe_wna16_status_string(99) == "unknown status"
 
@@ -232,3 +232,21 @@ def test_workspace_layout_consistent(lib):
     with pytest.raises(M.MoeWna16Error):
         M.moe_wna16_workspace_layout(4, 100, 2048, 256, 6)
     assert lib.moe_wna16_workspace_layout(4, 4096, 2048, 256, 6, None) == Bd.EINVAL
+
+
+def test_noalloc_rejects_oversized_calls_before_touching_the_device(lib):
+    """The scratch-size check runs with the other host checks (no GPU here):
+    a 2048-token prefill-shaped call needs more than 32 MiB."""
+    fake = 1 << 20   # aligned, never dereferenced: the call returns first
+    st = lib.moe_wna16_forward_noalloc(fake, fake, fake, fake, fake, fake, fake, 2048, 4096, 2048,
+                                       256, 6, Bd.QParams(2, 128), Bd.QParams(2, 128), 1.0, 0.0,
+                                       math.inf, fake, None)
+    assert st == Bd.ESCRATCH
+    assert "32 MiB" in M.moe_wna16_status_string(Bd.ESCRATCH)
+    # bad arguments are still EINVAL / EALIGN first
+    assert lib.moe_wna16_forward_noalloc(None, fake, fake, fake, fake, fake, fake, 4, 4096, 2048,
+                                         256, 6, Bd.QParams(2, 128), Bd.QParams(2, 128), 1.0, 0.0,
+                                         math.inf, fake, None) == Bd.EINVAL
+    assert lib.moe_wna16_forward_noalloc(fake + 2, fake, fake, fake, fake, fake, fake, 4, 4096,
+                                         2048, 256, 6, Bd.QParams(2, 128), Bd.QParams(2, 128),
+                                         1.0, 0.0, math.inf, fake, None) == Bd.EALIGN

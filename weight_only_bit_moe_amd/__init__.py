@@ -8,14 +8,14 @@ include/moe_wna16.h (libmoe_wna16.so, built in-tree by
 from .binding import (EXPORTED, LIB_PATH, MoeWna16Error, align, forward, load_library,
                       moe_wna16_align, moe_wna16_forward, moe_wna16_forward_profiled,
                       moe_wna16_plan, moe_wna16_quantize, quantize, moe_wna16_prepare,
-                      moe_wna16_forward_prepared, prepare,
+                      moe_wna16_forward_prepared, moe_wna16_forward_noalloc, prepare,
                       moe_wna16_status_string, moe_wna16_workspace_f32_offset,
                       moe_wna16_workspace_layout, moe_wna16_workspace_size, workspace_f32_sum,
                       workspace_for, workspace_meta, workspace_sort)
 
 __all__ = ["EXPORTED", "LIB_PATH", "MoeWna16Error", "align", "forward", "load_library",
            "moe_wna16_align", "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_plan", "moe_wna16_quantize", "quantize",
-           "moe_wna16_prepare", "moe_wna16_forward_prepared", "prepare",
+           "moe_wna16_prepare", "moe_wna16_forward_prepared", "moe_wna16_forward_noalloc", "prepare",
            "moe_wna16_status_string",
            "moe_wna16_workspace_f32_offset", "moe_wna16_workspace_layout",
            "moe_wna16_workspace_size", "workspace_f32_sum", "workspace_for", "workspace_meta",

@@ -15,14 +15,14 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_wna16.so")
 
-OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EARCH, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 
 #: every symbol include/moe_wna16.h declares
 EXPORTED = ("moe_wna16_workspace_size", "moe_wna16_workspace_f32_offset",
             "moe_wna16_workspace_layout", "moe_wna16_plan",
             "moe_wna16_forward", "moe_wna16_forward_profiled", "moe_wna16_align",
             "moe_wna16_quantize", "moe_wna16_prepare", "moe_wna16_forward_prepared",
-            "moe_wna16_status_string")
+            "moe_wna16_forward_noalloc", "moe_wna16_status_string")
 
 
 class QParams(ctypes.Structure):
@@ -82,6 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_wna16_prepare.restype = i
     lib.moe_wna16_forward_prepared.argtypes = lib.moe_wna16_forward.argtypes + [P]
     lib.moe_wna16_forward_prepared.restype = i
+    lib.moe_wna16_forward_noalloc.argtypes = lib.moe_wna16_forward.argtypes[:18] + [P]
+    lib.moe_wna16_forward_noalloc.restype = i
     lib.moe_wna16_status_string.argtypes = [i]
     lib.moe_wna16_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -192,6 +194,16 @@ def moe_wna16_forward_prepared(x, topk_ids, topk_w, w13_prepared, w13_scales, w2
         x, topk_ids, topk_w, w13_prepared, w13_scales, w2_prepared, w2_scales, T, H, I, E, topk,
         QParams(*q13), QParams(*q2), alpha, beta, clamp, out, workspace, workspace_bytes, stream,
         events)
+
+
+def moe_wna16_forward_noalloc(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed,
+                              w2_scales, T, H, I, E, topk, q13, q2, alpha, beta, clamp, out,
+                              stream) -> int:
+    """Raw entry point without a workspace (the library's per-GPU scratch);
+    returns the status."""
+    return load_library().moe_wna16_forward_noalloc(
+        x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H, I, E, topk,
+        QParams(*q13), QParams(*q2), alpha, beta, clamp, out, stream)
 
 
 def moe_wna16_prepare(packed, E, rows, K, q, prepared_out, stream) -> int:

@@ -51,12 +51,14 @@ struct Layout {
         tdone, total;
 };
 
-Layout layout_of(int T, int H, int I, int E, int topk)
+// Workspace pieces for tiles of at most `bm` rows (the sort's padded slots
+// and the act rows they index are bounded by P + bm * min(E, P)).
+Layout layout_for(int T, int H, int I, int E, int topk, int bm)
 {
     const size_t P = (size_t)T * topk;
     const size_t minEP = (size_t)E < P ? (size_t)E : P;
-    const size_t max_tiles = P / 4 + minEP + 1;        // smallest block_m (4) bound
-    const size_t max_slots = P + kMaxBlockM * minEP;   // covers every block_m <= 64
+    const size_t max_tiles = P / 4 + minEP + 1;   // smallest block_m (4) bound
+    const size_t max_slots = P + (size_t)bm * minEP;
     Layout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -79,6 +81,12 @@ Layout layout_of(int T, int H, int I, int E, int topk)
     L.tdone = take(max_tiles * 64);   // one counter per tile, 64 bytes apart
     L.total = o;
     return L;
+}
+
+// The caller-provided workspace covers every block_m <= 64 (any bits / group).
+Layout layout_of(int T, int H, int I, int E, int topk)
+{
+    return layout_for(T, H, I, E, topk, kMaxBlockM);
 }
 
 // Tiling: a pure function of the shapes.
@@ -141,6 +149,32 @@ int check_device()
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_WNA16_OK : MOE_WNA16_EHIP; }
 
+// The workspace of moe_wna16_forward_noalloc: one array per device, held
+// until the process ends, shared by every such call on that device (the
+// route kernel clears what must start at zero on every call).  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the
+// device address that hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> g_scratch[64];
+
+// Device address of the current device's scratch array (the device was
+// checked by check_device, so its index is below 64).
+int scratch_of_current_device(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_WNA16_EHIP;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_WNA16_EHIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return MOE_WNA16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +191,9 @@ const char *moe_wna16_status_string(int status)
     case MOE_WNA16_EWORKSPACE: return "workspace too small";
     case MOE_WNA16_EARCH: return "current device is not gfx950 (MI355X)";
     case MOE_WNA16_EHIP: return "HIP runtime error";
+    case MOE_WNA16_ESCRATCH:
+        return "call needs more workspace than moe_wna16_forward_noalloc's 32 MiB scratch "
+               "(use moe_wna16_forward with a workspace)";
     default: return "unknown status";
     }
 }
@@ -216,13 +253,16 @@ int moe_wna16_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
     return MOE_WNA16_OK;
 }
 
+// noalloc: the workspace is the library's own per-device scratch array
+// (workspace and workspace_bytes are ignored), laid out for the plan's tile
+// size; calls that need more than the array return ESCRATCH.
 static int forward_impl(const void *x, const int32_t *topk_ids, const float *topk_w,
                       const int32_t *w13_packed, const uint16_t *w13_scales,
                       const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H, int I,
                       int E, int topk, moe_wna16_qparams q13, moe_wna16_qparams q2, float alpha,
                       float beta, float clamp, void *out, void *workspace,
                       size_t workspace_bytes, hipStream_t stream,
-                      const hipEvent_t *events, bool prepared)
+                      const hipEvent_t *events, bool prepared, bool noalloc = false)
 {
     int st = check_sizes(T, H, I, E, topk);
     if (st != MOE_WNA16_OK)
@@ -236,23 +276,28 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     if (T == 0)
         return MOE_WNA16_OK;
     if (!x || !topk_ids || !topk_w || !w13_packed || !w13_scales || !w2_packed || !w2_scales ||
-        !out || !workspace)
+        !out || (!workspace && !noalloc))
         return MOE_WNA16_EINVAL;
     if (!aligned(x, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16) ||
-        !aligned(out, 16) || !aligned(workspace, kRegionAlign) || !aligned(topk_ids, 4) ||
-        !aligned(topk_w, 4) || !aligned(w13_scales, 2) || !aligned(w2_scales, 2))
+        !aligned(out, 16) || (!noalloc && !aligned(workspace, kRegionAlign)) ||
+        !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(w13_scales, 2) ||
+        !aligned(w2_scales, 2))
         return MOE_WNA16_EALIGN;
-    const Layout L = layout_of(T, H, I, E, topk);
-    if (workspace_bytes < L.total)
-        return MOE_WNA16_EWORKSPACE;
-    st = check_device();
-    if (st != MOE_WNA16_OK)
-        return st;
-
     moe_wna16_plan_t plan;
     make_plan(T, H, I, E, topk, q13, q2, &plan);
     if (prepared && (plan.w13_variant != 2 || plan.w2_variant != 2))
         return MOE_WNA16_EUNSUPPORTED;   // prepared codes feed the decode-shaped kernels only
+    const Layout L = noalloc ? layout_for(T, H, I, E, topk, plan.block_m)
+                             : layout_of(T, H, I, E, topk);
+    if (noalloc && L.total > kScratchBytes)
+        return MOE_WNA16_ESCRATCH;
+    if (!noalloc && workspace_bytes < L.total)
+        return MOE_WNA16_EWORKSPACE;
+    st = check_device();
+    if (st != MOE_WNA16_OK)
+        return st;
+    if (noalloc && (st = scratch_of_current_device(&workspace)) != MOE_WNA16_OK)
+        return st;
     LayerDims d{};
     d.T = T;
     d.H = H;
@@ -369,6 +414,18 @@ int moe_wna16_forward_prepared(const void *x, const int32_t *topk_ids, const flo
     return forward_impl(x, topk_ids, topk_w, w13_prepared, w13_scales, w2_prepared, w2_scales, T,
                         H, I, E, topk, q13, q2, alpha, beta, clamp, out, workspace,
                         workspace_bytes, stream, events, true);
+}
+
+int moe_wna16_forward_noalloc(const void *x, const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *w13_packed, const uint16_t *w13_scales,
+                              const int32_t *w2_packed, const uint16_t *w2_scales, int T, int H,
+                              int I, int E, int topk, moe_wna16_qparams q13,
+                              moe_wna16_qparams q2, float alpha, float beta, float clamp,
+                              void *out, hipStream_t stream)
+{
+    return forward_impl(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
+                        I, E, topk, q13, q2, alpha, beta, clamp, out, nullptr, 0, stream,
+                        nullptr, false, true);
 }
 
 int moe_wna16_prepare(const int32_t *packed, int E, int rows, int K, moe_wna16_qparams q,
