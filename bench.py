@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-decode-extra", dest="decode_extra", action="store_false",
                     help="do not add the decode workload's figures to a prefill line")
+    ap.add_argument("--no-shards", dest="shards", action="store_false",
+                    help="do not add the one-GPU shares of the sharded layer (expert "
+                         "parallelism 8, tensor parallelism 4) to a prefill line")
     ap.add_argument("--batches", type=int, default=64,
                     help="distinct routing batches cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -174,6 +177,19 @@ def main():
             "value", "unit", "ms_per_step", "steps", "warmup", "config", "roofline", "kernel_ms",
             "step_ms_percentiles", "layer_hbm_gbs", "layer_hbm_frac", "experts_touched_per_step",
             "algorithmic_bytes")}
+    if args.shards and cfg not in (2, 3):
+        # one GPU's share of the sharded layer at its real shape: expert
+        # parallelism over 8 GPUs (32 local experts) and tensor parallelism
+        # over 4 (intermediate 512), for the decode and 2048-token workloads
+        from weight_only_bit_moe_amd.inputs import shard_spec
+        result["shards"] = {}
+        for c in (2, 4):
+            for sh in ("ep8", "tp4"):
+                r, _ = measure_layer(c, args, None, None, "auto", spec=shard_spec(c, sh))
+                result["shards"][r["config"]["workload"]] = {k: r[k] for k in (
+                    "value", "unit", "ms_per_step", "steps", "warmup", "roofline", "kernel_ms",
+                    "layer_hbm_frac", "layer_mfma_frac", "experts_touched_per_step",
+                    "pairs_per_step")}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     else:
@@ -188,14 +204,15 @@ def percentiles(v):
             "p90": float(np.percentile(a, 90))}
 
 
-def measure_layer(cfg, args, steps, warmup, codes):
-    """Time `steps` layer calls on workload `cfg` after `warmup` untimed ones.
-    Returns (the JSON dict of the measurement, the host layer)."""
+def measure_layer(cfg, args, steps, warmup, codes, spec=None):
+    """Time `steps` layer calls on workload `cfg` (or `spec`, drawn with seed
+    `cfg`) after `warmup` untimed ones.  Returns (the JSON dict of the
+    measurement, the host layer)."""
     import numpy as np
     import torch
 
     import weight_only_bit_moe_amd as M
-    from weight_only_bit_moe_amd.inputs import make_batch, make_config
+    from weight_only_bit_moe_amd.inputs import make_batch, make_config, make_layer
 
     decode = cfg in (2, 3)
     # Decode steps are ~40 us: a few hundred untimed calls bring the host's
@@ -206,7 +223,7 @@ def measure_layer(cfg, args, steps, warmup, codes):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    L = make_config(cfg)
+    L = make_config(cfg) if spec is None else make_layer(spec, cfg)
     sp = L.spec
     T, H, I, E, k = sp.T, sp.H, sp.I, sp.E, sp.topk
     P = T * k
@@ -312,13 +329,16 @@ def measure_layer(cfg, args, steps, warmup, codes):
     # (read by w13) + out (written after w2); flops = 2 P (2I H + H I)
     b13 = per_expert_bytes(sp.bits13, sp.group13, 2 * I, H)
     b2 = per_expert_bytes(sp.bits2, sp.group2, H, I)
-    touched = []
+    touched, pairs = [], []
     for i in range(steps):
         ids = host_batches[i % nb][0]
-        touched.append(len(np.unique(ids[(ids >= 0) & (ids < E)])))
+        local = ids[(ids >= 0) & (ids < E)]
+        touched.append(len(np.unique(local)))
+        pairs.append(local.size)   # pairs routed to this layer's experts
     mean_touched = float(np.mean(touched))
+    Pl = float(np.mean(pairs))
     alg_bytes = {"w13": mean_touched * b13 + T * H * 2, "w2": mean_touched * b2 + T * H * 2}
-    alg_flops = {"w13": 2.0 * P * 2 * I * H, "w2": 2.0 * P * H * I}
+    alg_flops = {"w13": 2.0 * Pl * 2 * I * H, "w2": 2.0 * Pl * H * I}
     alg_bytes["w13+w2"] = alg_bytes["w13"] + alg_bytes["w2"]
     alg_flops["w13+w2"] = alg_flops["w13"] + alg_flops["w2"]
     layer_bytes = alg_bytes["w13+w2"]
@@ -360,6 +380,7 @@ def measure_layer(cfg, args, steps, warmup, codes):
         "dtype": "bf16",
         "data": "synthetic (seeded; fresh routing batch per step)",
         "config": {"workload": sp.name, "T": T, "hidden": H, "intermediate": I, "experts": E,
+                   "routing_experts": sp.routing_experts or E,
                    "topk": k, "w13": f"W{sp.bits13} g{sp.group13}",
                    "w2": f"W{sp.bits2} g{sp.group2}", "block_m": plan["block_m"],
                    "codes": "prepared order" if prepared else "checkpoint order",
@@ -381,6 +402,7 @@ def measure_layer(cfg, args, steps, warmup, codes):
         "layer_mfma_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "layer_mfma_frac": layer_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "experts_touched_per_step": mean_touched,
+        "pairs_per_step": Pl,
     }
     del batches, w13, w2, s13, s2, ws, out
     torch.cuda.empty_cache()

@@ -18,7 +18,8 @@ import torch
 import weight_only_bit_moe_amd as M
 from oracle import oracle as O
 from tests import _gpu as G
-from weight_only_bit_moe_amd.inputs import CONFIGS, LayerSpec, make_config, make_layer
+from weight_only_bit_moe_amd.inputs import (CONFIGS, LayerSpec, make_config, make_layer,
+                                            shard_spec)
 
 pytestmark = pytest.mark.gpu
 
@@ -398,6 +399,27 @@ def test_full_workload_sampled_tokens(dev, cfg):
     assert len(rows) == min(sp.T, 64)
     ref = O.forward_layer(L, tokens=rows)
     G.assert_parity(y[rows], ref, f"config {cfg}")
+
+
+@pytest.mark.parametrize("shard", ["ep8", "tp4"])
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_one_gpu_share_of_sharded_layer(dev, cfg, shard):
+    """One GPU's share of the sharded layer at its real shape: expert
+    parallelism over 8 GPUs (32 local experts receiving the global top-k ids
+    over 256 experts; the other ids contribute nothing here) and tensor
+    parallelism over 4 (intermediate 512), for the decode and the 2048-token
+    prefill workloads.  The partial sums of the shares are what the
+    cross-GPU reduction would add."""
+    sp = shard_spec(cfg, shard)
+    L = make_layer(sp, seed=cfg)
+    print(f"{sp.name}: T={sp.T} E={sp.E} I={sp.I} k={sp.topk}", flush=True)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    _, y = G.run_layer(L, dev, workspace=ws)
+    rows = list(range(sp.T)) if sp.T <= 64 else sampled_tokens(L, ws)
+    G.assert_parity(y[rows], O.forward_layer(L, tokens=rows), sp.name)
+    if shard == "ep8":
+        local = (L.topk_ids >= 0) & (L.topk_ids < sp.E)
+        assert G.layer_sort(L, ws)[1]["bad_ids"] == int((~local).sum())
 
 
 @pytest.mark.parametrize("T,k,routing,bad", [(896, 8, "zipf", False), (7169, 1, "uniform", True),

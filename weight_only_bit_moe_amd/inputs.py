@@ -37,6 +37,8 @@ __all__ = [
     "make_layer",
     "make_batch",
     "make_config",
+    "SHARDS",
+    "shard_spec",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "QuantSpec",
@@ -72,6 +74,11 @@ class LayerSpec:
     alpha: float = 1.0
     beta: float = 0.0
     clamp: float = math.inf
+    # experts the routing draws from (0: E).  With more than E, the layer is
+    # one GPU's share of an expert-parallel layer: it holds experts [0, E)
+    # and receives the tokens' global top-k ids, the others belonging to
+    # other GPUs.
+    routing_experts: int = 0
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)
@@ -138,7 +145,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _routing_ids(rng: np.random.Generator, spec: LayerSpec) -> np.ndarray:
-    T, E, k = spec.T, spec.E, spec.topk
+    T, k = spec.T, spec.topk
+    E = spec.routing_experts or spec.E
     if k > E:
         raise ValueError("distinct top-k routing needs topk <= E")
     if spec.routing == "uniform":
@@ -231,6 +239,21 @@ CONFIGS = {
                  scale_dist="loguniform", x_sigma=2.0, outlier_frac=0.01, alpha=1.702,
                  beta=1.0, clamp=7.0),
 }
+
+
+#: One GPU's share of the decode and prefill-chunk workloads when the layer is
+#: sharded: expert parallelism over 8 GPUs (32 local experts, the routing over
+#: all 256) and tensor parallelism over 4 (intermediate 512 of 2048 per GPU:
+#: its slice of every expert's gate, up and down rows).
+SHARDS = {
+    "ep8": dict(E=32, routing_experts=256),
+    "tp4": dict(I=512),
+}
+
+
+def shard_spec(idx: int, shard: str) -> LayerSpec:
+    sp = CONFIGS[idx]
+    return sp.replace(name=f"{sp.name}-{shard}", **SHARDS[shard])
 
 
 def make_config(idx: int, seed: Optional[int] = None) -> Layer:
