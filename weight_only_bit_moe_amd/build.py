@@ -59,6 +59,55 @@ def build(verbose: bool = False, jobs: int = 3) -> str:
     return LIB
 
 
+# Host-side sanitizer build: the C ABI's host code (api.hip) and the oracle's C
+# code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer, linked
+# with the other library objects into tests/sanitize/host_check (no GPU needed).
+SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+       "-fno-omit-frame-pointer"]
+SAN_DRIVER = os.path.join(ROOT, "tests", "sanitize", "host_check.cpp")
+SAN_EXE = os.path.join(ROOT, "tests", "sanitize", "host_check")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build tests/sanitize/host_check; returns its path."""
+    llvm = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin")
+    clang = os.path.join(llvm, "clang")
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(bdir, src + ".o")
+        if src == "api.hip":
+            obj = os.path.join(bdir, "api.san.o")
+            # device code as usual; every sanitizer flag applies to the host pass only
+            host = [f for flag in SAN for f in ("-Xarch_host", flag)]
+            _run([hipcc()] + flags() + host + ["-g", "-c", os.path.join(CSRC, src), "-o", obj],
+                 verbose)
+        elif not os.path.exists(obj):
+            _run([hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    oracle_obj = os.path.join(bdir, "moe_oracle.san.o")
+    _run([clang, "-std=c99", "-O1", "-g", "-fPIC"] + SAN +
+         ["-c", os.path.join(ROOT, "oracle", "moe_oracle.c"), "-o", oracle_obj], verbose)
+    driver_obj = os.path.join(bdir, "host_check.san.o")
+    _run([clang + "++", "-std=c++17", "-O1", "-g", "-D__HIP_PLATFORM_AMD__",
+          "-I", "/opt/rocm/include", "-I", INCLUDE] + SAN +
+         ["-c", SAN_DRIVER, "-o", driver_obj], verbose)
+    _run([clang + "++"] + SAN + ["-o", SAN_EXE, driver_obj, oracle_obj] + objs +
+         ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-lm"], verbose)
+    return SAN_EXE
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    text = "\n".join(l for l in r.stdout.decode(errors="replace").splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{text}")
+
+
 def _drain(procs):
     while procs:
         cmd, p = procs.pop(0)
@@ -73,4 +122,7 @@ def _drain(procs):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))
