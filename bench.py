@@ -303,14 +303,18 @@ def measure_layer(cfg, args, steps, warmup, codes, spec=None):
     if meta[2] != 0:
         raise RuntimeError(f"{meta[2]} fused decode waits gave up: the output is unreliable")
 
-    # one entry per launch: steps that share a launch (plan: gemms_one_launch,
-    # convert_in_w2) are timed as that launch; with 64-row tiles the routing
-    # step also holds the split of the tile kernels' items over the XCDs
+    # one entry per launch: steps that share a launch (plan: single_launch,
+    # gemms_one_launch, convert_in_w2) are timed as that launch; with 64-row
+    # tiles the routing step also holds the split of the tile kernels' items
+    # over the XCDs
     one = bool(plan["gemms_one_launch"])
-    launches = [("route" if decode_shaped else "route+split", 0, 1)]
-    launches += [("w13+w2", 2, 5)] if one else [("w13", 2, 3), ("w2", 4, 5)]
-    if not plan["convert_in_w2"]:
-        launches.append(("convert", 6, 7))
+    if plan["single_launch"]:
+        launches = [("layer", 0, 5)]
+    else:
+        launches = [("route" if decode_shaped else "route+split", 0, 1)]
+        launches += [("w13+w2", 2, 5)] if one else [("w13", 2, 3), ("w2", 4, 5)]
+        if not plan["convert_in_w2"]:
+            launches.append(("convert", 6, 7))
     kern_ms = {name: [] for name, _, _ in launches}
     step_gpu_ms = []
     last_stop = launches[-1][2]
@@ -341,13 +345,15 @@ def measure_layer(cfg, args, steps, warmup, codes, spec=None):
     alg_flops = {"w13": 2.0 * Pl * 2 * I * H, "w2": 2.0 * Pl * H * I}
     alg_bytes["w13+w2"] = alg_bytes["w13"] + alg_bytes["w2"]
     alg_flops["w13+w2"] = alg_flops["w13"] + alg_flops["w2"]
+    alg_bytes["layer"] = alg_bytes["w13+w2"]   # the single launch: the routing reads ids only
+    alg_flops["layer"] = alg_flops["w13+w2"]
     layer_bytes = alg_bytes["w13+w2"]
     layer_flops = alg_flops["w13+w2"]
     # traffic of this implementation outside those bytes (not algorithmic):
     # act written by w13 and read by w2, the FP32 sum (atomics, then rounding)
     impl_bytes = {"act_write_read": 2.0 * P * I * 2, "fp32_sum": 3.0 * T * H * 4}
 
-    dom = max((n for n in avg if n.startswith("w")), key=lambda n: avg[n])
+    dom = max((n for n in avg if n.startswith("w") or n == "layer"), key=lambda n: avg[n])
     if decode:
         achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -25,7 +25,15 @@
  *   - Work is enqueued asynchronously on `stream`; no entry point
  *     synchronises the host.  The enqueued work is kernels only (no memset
  *     or copy nodes), so the calls can be captured into a HIP graph and
- *     replayed; the layer keeps no state in the workspace between calls.
+ *     replayed.
+ *   - Workspace state: the first MOE_WNA16_SYNC_BYTES bytes of a forward
+ *     workspace hold counters that the single-launch decode plan
+ *     (moe_wna16_plan_t.single_launch) uses to order its workgroups.  They
+ *     must be zero before a workspace's first forward call (allocate it
+ *     zeroed, or clear them once); every call leaves them zero, except a
+ *     call whose status word meta[2] (moe_wna16_workspace_layout) reports
+ *     waits that gave up: clear them again before reusing that workspace.
+ *     Nothing else carries over between calls.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     non-zero status means nothing was launched and no buffer was touched.
  *   - Device-side values (expert ids) are not validated on the host: an id
@@ -54,6 +62,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Leading bytes of a forward workspace that must be zero before its first use. */
+#define MOE_WNA16_SYNC_BYTES 32768
 
 typedef enum {
     MOE_WNA16_OK = 0,
@@ -84,6 +95,10 @@ typedef struct {
                               /*    (same bits and group on both projections)      */
     int32_t convert_in_w2;  /* 1: the BF16 rounding runs inside the decode w2       */
                             /*    launch (decode shapes with T*H <= 2^18)          */
+    int32_t single_launch;  /* 1: the whole layer (routing, reorder, both GEMMs,    */
+                            /*    rounding) is one launch: gemms_one_launch and     */
+                            /*    convert_in_w2 with T*topk <= 64, max_tiles <= 128 */
+                            /*    and H <= 16384                                    */
 } moe_wna16_plan_t;
 
 /*
@@ -141,8 +156,9 @@ int moe_wna16_forward(const void *x, const int32_t *topk_ids, const float *topk_
  * convert_in_w2): the launch records the first step's start event and the
  * last step's stop event, and the events in between are not recorded; so
  * with gemms_one_launch, events[2] and events[5] bracket the one w13 + w2
- * launch, and with convert_in_w2, events[6] and events[7] stay unrecorded
- * (the rounding is inside the w2 launch).  Same checks and status codes as
+ * launch, with convert_in_w2, events[6] and events[7] stay unrecorded
+ * (the rounding is inside the w2 launch), and with single_launch only
+ * events[0] and events[5] are recorded, around the one launch.  Same checks and status codes as
  * moe_wna16_forward, plus EINVAL for a NULL `events`.
  */
 int moe_wna16_forward_profiled(const void *x, const int32_t *topk_ids, const float *topk_w,
@@ -203,11 +219,15 @@ int moe_wna16_workspace_f32_offset(int T, int H, int I, int E, int topk, size_t 
  *                   [2] fused decode waits that gave up: 0 after a normal call.  In
  *                       the one-launch decode plan (moe_wna16_plan_t.gemms_one_launch)
  *                       each down-projection workgroup waits, with a bounded spin, for
- *                       the gate/up workgroups of its tile; a non-zero count means a
- *                       wait ended at its bound and that call's output is unreliable
+ *                       the gate/up workgroups of its tile, and in the single-launch
+ *                       plan each gate/up workgroup also waits for the routing
+ *                       workgroups; a non-zero count means a wait ended at its bound,
+ *                       that call's output is unreliable and the workspace's first
+ *                       MOE_WNA16_SYNC_BYTES bytes must be cleared before its next use
  *                   [3..7] reserved, [8..25] the prefill tile kernels' split of their
  *                       (tile, column block) items over the 8 XCDs (gate/up then down:
- *                       8 range starts and the item count each)
+ *                       8 range starts and the item count each); bytes [256,
+ *                       MOE_WNA16_SYNC_BYTES) hold the single-launch counters
  *   expert_offsets  int32 [E + 1]     \
  *   sorted_ids      int32 [num_tiles * block_m]   the tile layout of
  *   tile_expert     int32 [num_tiles]             moe_wna16_align, with the

@@ -66,9 +66,18 @@ def run_layer(L, dev, d=None, out=None, workspace=None, prepared=False, check_so
     assert np.array_equal(bits, f32_to_bf16_bits(f32)), "BF16 output is not RNE(FP32 sum)"
     meta = M.workspace_meta(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
     assert meta[2] == 0, f"{meta[2]} fused decode waits gave up"
+    assert_sync_clear(workspace, sp)
     if check_sort:
         assert_layer_sort(L, workspace)
     return y, f32.astype(np.float64)
+
+
+def assert_sync_clear(workspace, sp):
+    """The single-launch decode's counters (workspace bytes [256,
+    SYNC_BYTES) past the status words) are back at zero after a call."""
+    at = M.moe_wna16_workspace_layout(sp.T, sp.H, sp.I, sp.E, sp.topk)["meta"]
+    sync = workspace[at + 256:at + M.SYNC_BYTES].cpu().numpy()
+    assert not sync.any(), f"sync counters left non-zero at bytes {np.flatnonzero(sync)[:8]}"
 
 
 def layer_sort(L, workspace):

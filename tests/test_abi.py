@@ -54,10 +54,11 @@ def test_plan_picks_tiles_from_rows_per_expert(lib):
     dec = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (2, 128), (2, 128))
     bdec = M.moe_wna16_plan(64, 4096, 2048, 256, 6, (4, 128), (4, 128))
     pre = M.moe_wna16_plan(2048, 4096, 2048, 256, 6, (2, 128), (2, 128))
-    assert dec["block_m"] == 4 and dec["w13_variant"] == 2 and dec["max_tiles"] == 24 // 4 + 24
+    # tile capacity: sum over used experts of ceil(count / bm) <= (P + (bm - 1) min(E, P)) / bm
+    assert dec["block_m"] == 4 and dec["w13_variant"] == 2 and dec["max_tiles"] == 24
     assert bdec["block_m"] == 4 and bdec["w2_variant"] == 2
     assert pre["block_m"] == 64 and pre["w2_variant"] == 1
-    assert pre["max_tiles"] == 2048 * 6 // 64 + 256
+    assert pre["max_tiles"] == (2048 * 6 + 63 * 256) // 64
     # the decode kernel's LDS image must fit: a 32-group w13 at H=4096 goes prefill-shaped
     big = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (4, 32), (2, 128))
     assert big["w13_variant"] == 1
@@ -76,6 +77,15 @@ def test_plan_reports_shared_launches(lib):
     assert g32["w13_variant"] == 2 and g32["gemms_one_launch"] == 0
     pre = M.moe_wna16_plan(2048, 4096, 2048, 256, 6, (2, 128), (2, 128))
     assert pre["gemms_one_launch"] == 0 and pre["convert_in_w2"] == 0
+    # the whole layer in one launch: both shared launches and at most 64 pairs
+    assert dec["single_launch"] == 1
+    assert bdec["single_launch"] == 0                        # 384 pairs
+    edge = M.moe_wna16_plan(8, 4096, 2048, 256, 8, (4, 128), (4, 128))
+    assert edge["single_launch"] == 1                        # exactly 64 pairs
+    over = M.moe_wna16_plan(13, 4096, 2048, 256, 5, (4, 128), (4, 128))
+    assert over["gemms_one_launch"] == 1 and over["single_launch"] == 0   # 65 pairs
+    for p in (mixed, g32, pre, big_t):
+        assert p["single_launch"] == 0
 
 
 NAN, INF = float("nan"), math.inf

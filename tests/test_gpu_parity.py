@@ -286,6 +286,8 @@ def test_profiled_entry_matches_plain_and_records_events(dev, T, E, HI, q):
     launches = [(0, 1)] + ([(2, 5)] if plan["gemms_one_launch"] else [(2, 3), (4, 5)])
     if not plan["convert_in_w2"]:
         launches.append((6, 7))
+    if plan["single_launch"]:
+        launches = [(0, 5)]
     for a0, a1 in launches:
         assert hip.elapsed_ms(ev[a0], ev[a1]) >= 0.0
     for (_, a1), (b0, _) in zip(launches, launches[1:]):
@@ -334,6 +336,64 @@ def test_reused_workspace_and_output(dev):
     G.run_layer(big, dev, workspace=ws, out=out)
     _, y = G.run_layer(small, dev, workspace=ws, out=out[:6])
     G.assert_parity(y, O.forward_layer(small), "reuse")
+
+
+@pytest.mark.parametrize("q", [(2, 64), (2, 128), (4, 32), (4, 64), (4, 128)])
+def test_single_launch_back_to_back_calls(dev, q):
+    """The single-launch decode plan (routing, reorder, zeroing, both GEMMs
+    and the rounding in one launch, ordered by counters in the workspace):
+    four calls enqueued back to back on one workspace, without a host sync
+    in between, with plain, duplicate, partly invalid and all-invalid ids;
+    each call's output (kept in its own buffer) matches the oracle, and the
+    counters are back at zero afterwards."""
+    sp = spec(T=8, H=1024, I=1024, E=16, topk=8, bits13=q[0], group13=q[1], bits2=q[0],
+              group2=q[1], **ACT)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, q, q)
+    assert plan["single_launch"] == 1   # 64 pairs: the largest single-launch batch
+    layers = []
+    for seed, kind in ((90, "plain"), (91, "dup"), (92, "bad"), (93, "allbad")):
+        L = make_layer(sp, seed=seed)
+        if kind == "dup":
+            L.topk_ids[:, 1] = L.topk_ids[:, 0]
+            L.topk_ids[2, :] = L.topk_ids[2, 0]   # one expert holds all of token 2's slots
+        elif kind == "bad":
+            L.topk_ids[1, :] = -1
+            L.topk_ids[5, 3] = sp.E
+        elif kind == "allbad":
+            L.topk_ids[:, :] = sp.E + 1
+        layers.append(L)
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    outs = []
+    for L in layers:
+        d = G.to_device(L, dev)
+        outs.append(M.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["s13"], d["w2"],
+                              d["s2"], bits=(q[0], q[0]), group=(q[1], q[1]), alpha=sp.alpha,
+                              beta=sp.beta, clamp=sp.clamp, workspace=ws))
+    torch.cuda.synchronize(dev)
+    meta = M.workspace_meta(ws, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
+    assert meta[2] == 0
+    G.assert_sync_clear(ws, sp)
+    G.assert_layer_sort(layers[-1], ws)
+    for L, y in zip(layers, outs):
+        G.assert_parity(G.to_f64(y), O.forward_layer(L), "single launch")
+    assert not G.to_f64(outs[-1]).any()
+
+
+@pytest.mark.parametrize("T", [8, 40])
+@pytest.mark.parametrize("prepared", [False, True])
+def test_decode_w2g128_i2048(dev, T, prepared):
+    """2-bit group-128 decode at I = 2048 (the decode workloads' format and
+    intermediate size), checkpoint and prepared codes, in the single launch
+    (16 pairs) and in the shared w13 + w2 launch (80 pairs)."""
+    sp = spec(T=T, H=1024, I=2048, E=32, topk=2, bits13=2, bits2=2, scale_lo=0.01,
+              scale_hi=0.05, **ACT)
+    q = (2, 128)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, q, q)
+    assert plan["gemms_one_launch"] == 1
+    assert plan["single_launch"] == (1 if T * 2 <= 64 else 0)
+    L = make_layer(sp, seed=95 + T)
+    _, got = G.run_layer(L, dev, prepared=prepared)
+    G.assert_parity(got, O.forward_layer(L), "2-bit g128, I=2048")
 
 
 # --------------------------------------------------------------------------

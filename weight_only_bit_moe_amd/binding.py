@@ -32,7 +32,8 @@ class QParams(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
                 ("w13_variant", ctypes.c_int32), ("w2_variant", ctypes.c_int32),
-                ("gemms_one_launch", ctypes.c_int32), ("convert_in_w2", ctypes.c_int32)]
+                ("gemms_one_launch", ctypes.c_int32), ("convert_in_w2", ctypes.c_int32),
+                ("single_launch", ctypes.c_int32)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -164,7 +165,7 @@ def moe_wna16_plan(T, H, I, E, topk, q13: Tuple[int, int], q2: Tuple[int, int]) 
         raise MoeWna16Error(st, "moe_wna16_plan")
     return dict(block_m=plan.block_m, max_tiles=plan.max_tiles, w13_variant=plan.w13_variant,
                 w2_variant=plan.w2_variant, gemms_one_launch=plan.gemms_one_launch,
-                convert_in_w2=plan.convert_in_w2)
+                convert_in_w2=plan.convert_in_w2, single_launch=plan.single_launch)
 
 
 def moe_wna16_forward(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,
@@ -248,10 +249,16 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
+SYNC_BYTES = 32768   # MOE_WNA16_SYNC_BYTES: leading workspace bytes that start at zero
+
+
 def workspace_for(T, H, I, E, topk, device):
+    """A forward workspace for these sizes, zeroed (the single-launch decode's
+    counters at its start must be zero before the first call; every call
+    leaves them zero)."""
     torch = _torch()
     n = moe_wna16_workspace_size(T, H, I, E, topk)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, SYNC_BYTES), dtype=torch.uint8, device=device)
 
 
 def forward(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, *,

@@ -66,7 +66,10 @@ Layout layout_for(int T, int H, int I, int E, int topk, int bm)
         o = round_up(o + bytes, kRegionAlign);
         return at;
     };
-    L.meta = take((8 + 2 * wna16::kSplitEntries) * sizeof(int32_t));   // counts, then the XCD split
+    // status words, the XCD split, then the single-launch decode's counters
+    static_assert((8 + 2 * wna16::kSplitEntries) * sizeof(int32_t) <= wna16::kSyncPrepDone,
+                  "status words");
+    L.meta = take(wna16::kSyncBytes);
     L.offsets = take((size_t)(E + 1) * sizeof(int32_t));
     L.sorted = take(max_slots * sizeof(int32_t));
     L.tiles = take(max_tiles * sizeof(int32_t));
@@ -74,7 +77,8 @@ Layout layout_for(int T, int H, int I, int E, int topk, int bm)
     L.xperm = take((size_t)T * H * sizeof(uint16_t));
     L.xbias = take((size_t)T * (H / kMinGroup) * sizeof(float));
     L.act = take(max_slots * (size_t)I * sizeof(uint16_t));
-    L.actbias = take(max_slots * (size_t)(I / kMinGroup) * sizeof(float));
+    // (twice: the single-launch decode stores each group's term in two halves)
+    L.actbias = take(2 * max_slots * (size_t)(I / kMinGroup) * sizeof(float));
     L.outf32 = take((size_t)T * H * sizeof(float));
     L.ccounts = take((size_t)wna16::align_chunks((long long)P) * (E + 1) * sizeof(int32_t));
     L.done = take((size_t)H);   // one counter per 64 output columns, 64 bytes apart
@@ -107,12 +111,19 @@ void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
                         H % (512 / q13.bits) == 0 && I % (512 / q2.bits) == 0;
     const int bm = decode ? wna16::kDecodeRows : 64;
     plan->block_m = bm;
-    plan->max_tiles = (int)(P / bm + (E < P ? E : P));
+    // tiles = sum over the used experts of ceil(count / bm) <= (P + (bm - 1) * used) / bm
+    plan->max_tiles = (int)((P + (long long)(bm - 1) * (E < P ? E : P)) / bm);
     plan->w13_variant = decode ? 2 : 1;
     plan->w2_variant = decode ? 2 : 1;
     plan->gemms_one_launch =
         decode && wna16::decode_one_launch(q13.bits, q13.group, q2.bits, q2.group, H, I) ? 1 : 0;
     plan->convert_in_w2 = decode && (size_t)T * H <= wna16::kFusedConvertMax ? 1 : 0;
+    plan->single_launch = plan->gemms_one_launch && plan->convert_in_w2 &&
+                                  P <= wna16::kSingleLaunchPairs &&
+                                  plan->max_tiles <= wna16::kSyncTiles &&
+                                  H / 128 <= wna16::kSyncBlocks
+                              ? 1
+                              : 0;
 }
 
 // The prefill-shaped kernels address activations, their bias terms and one
@@ -333,12 +344,23 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.done = reinterpret_cast<int32_t *>(base + L.done);
     ws.tile_done = reinterpret_cast<int32_t *>(base + L.tdone);
     ws.xcd_first = ws.meta + 8;
+    ws.prep_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncPrepDone);
+    ws.blocks_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncBlocksDone);
+    ws.sync_tiles = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncTilesAt);
+    ws.sync_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncDoneAt);
 
     wna16::KernelEvents ev[4];
     if (events)
         for (int i = 0; i < 4; ++i)
             ev[i] = wna16::KernelEvents{events[2 * i], events[2 * i + 1]};
     const uint16_t *xb = static_cast<const uint16_t *>(x);
+    uint16_t *outb = static_cast<uint16_t *>(out);
+    // Small decode batches: the whole layer is one launch, which carries the
+    // routing step's start event and the down projection's stop event.
+    if (plan.single_launch)
+        return hip_status(wna16::launch_decode_layer(
+            xb, topk_ids, w13_packed, w13_scales, w2_packed, w2_scales, topk_w, d, ws, stream,
+            wna16::KernelEvents{ev[0].start, ev[2].stop}, outb));
     // Tile-kernel plans split the items over the XCDs right after the sort:
     // the split launch belongs to the routing step and carries its stop event.
     const bool split = plan.w13_variant == 1 || plan.w2_variant == 1;
@@ -355,7 +377,6 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     // entry launches the same kernels; a shared launch carries the first
     // step's start event and the last step's stop event, and the events in
     // between are not recorded.
-    uint16_t *outb = static_cast<uint16_t *>(out);
     const bool fuse = plan.convert_in_w2 != 0;
     if (plan.gemms_one_launch) {
         if ((st = hip_status(wna16::launch_decode(

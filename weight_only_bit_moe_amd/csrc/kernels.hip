@@ -258,7 +258,8 @@ __device__ __forceinline__ void wave_lds_sync()
 // count in LDS and later writes the expert's tiles and padding slots.  The
 // expert offsets are a wave-level exclusive scan over per-lane runs of
 // ceil(E / 64) consecutive experts.  No workgroup barrier is needed.
-__device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int P, int E, int bm,
+__device__ void align_wave(int *__restrict__ sh_cnt, int *__restrict__ sh_off,
+                           const int32_t *__restrict__ ids, int P, int E, int bm,
                            int32_t *__restrict__ sorted_ids, int32_t *__restrict__ tile_expert,
                            int32_t *__restrict__ offsets, int32_t *__restrict__ inv_perm,
                            int32_t *__restrict__ num_tiles, int32_t *__restrict__ bad_ids)
@@ -275,16 +276,16 @@ __device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int
     const int nbad = __popcll(__ballot(lane < P && !ok));
 
     for (int i = lane; i < E; i += 64)
-        sh.cnt[i] = 0;
+        sh_cnt[i] = 0;
     wave_lds_sync();
     if (leader)
-        sh.cnt[e] = padded;
+        sh_cnt[e] = padded;
     wave_lds_sync();
     const int per = (E + 63) / 64;
     const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
     int run = 0;
     for (int i = e0; i < e1; ++i)
-        run += sh.cnt[i];
+        run += sh_cnt[i];
     int incl = run;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -294,8 +295,8 @@ __device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int
     }
     int acc = incl - run;
     for (int i = e0; i < e1; ++i) {
-        const int c = sh.cnt[i];
-        sh.off[i] = acc;
+        const int c = sh_cnt[i];
+        sh_off[i] = acc;
         offsets[i] = acc;
         acc += c;
     }
@@ -307,7 +308,7 @@ __device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int
     }
     wave_lds_sync();
     if (ok) {
-        const int base = sh.off[e];
+        const int base = sh_off[e];
         sorted_ids[base + rank] = lane;
         inv_perm[lane] = base + rank;
         if (leader) {
@@ -321,6 +322,64 @@ __device__ void align_wave(AlignShared &sh, const int32_t *__restrict__ ids, int
     }
 }
 
+// The tile layout align_wave writes, for one tile only, computed by one wave
+// from the ids (P <= 64, lane p holds pair p): the tile count, the expert of
+// tile b (-1 past the last tile) and its kDecodeRows pair indices (P for
+// padding slots).  Every lane returns the same values.  Tiles list the
+// experts in ascending order, each expert's pairs in ascending pair order,
+// padded to multiples of 4 rows, so a pair's slot is (valid pairs with a
+// smaller id) + (padding of the smaller ids' experts) + (its rank among its
+// own id's pairs).  One pass over the 11 bits of the keys, most significant
+// first, with a ballot per bit, gives every lane the mask of lanes with a
+// smaller key and the mask of lanes with its own key; the padding of each
+// expert (0..3 rows) is counted with two more ballots over the experts' first
+// lanes.
+__device__ __forceinline__ void wave_tile_lookup(const int32_t *__restrict__ ids, int P, int E,
+                                                 int b, int &ntiles, int &expert,
+                                                 int (&pair)[kDecodeRows])
+{
+    static_assert(kDecodeRows == 4, "padding counted in two bits");
+    static_assert(kMaxExperts == 1024, "keys of 11 bits");
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int id = lane < P ? ids[lane] : -1;
+    const bool ok = lane < P && id >= 0 && id < E;
+    const int key = ok ? id : kMaxExperts;   // invalid lanes share the largest key
+    uint64_t less = 0, same = ~0ull;
+#pragma unroll
+    for (int bit = 10; bit >= 0; --bit) {
+        const bool mine = (key >> bit) & 1;
+        const uint64_t ones = __ballot(mine);
+        if (mine)
+            less |= same & ~ones;   // same prefix so far, 0 where this lane has 1
+        same &= mine ? ones : ~ones;
+    }
+    const uint64_t valid = __ballot(ok);
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    const bool leader = ok && rank == 0;
+    const int pad = leader ? (kDecodeRows - cnt % kDecodeRows) % kDecodeRows : 0;
+    const uint64_t pad1 = __ballot(pad & 1), pad2 = __ballot(pad & 2);
+    const int off = __popcll(less & valid) + __popcll(less & pad1) + 2 * __popcll(less & pad2);
+    ntiles = (__popcll(valid) + __popcll(pad1) + 2 * __popcll(pad2)) / kDecodeRows;
+    const int s0 = b * kDecodeRows;
+    const uint64_t own = __ballot(leader && off <= s0 && s0 < off + cnt + pad);
+    expert = -1;
+#pragma unroll
+    for (int r = 0; r < kDecodeRows; ++r)
+        pair[r] = P;
+    if (own != 0) {
+        const int L = __ffsll((unsigned long long)own) - 1;
+        expert = __builtin_amdgcn_readlane(key, L);
+        const int first = s0 - __builtin_amdgcn_readlane(off, L);   // rank of the tile's slot 0
+#pragma unroll
+        for (int r = 0; r < kDecodeRows; ++r) {
+            const uint64_t hit = __ballot(key == expert && rank == first + r);
+            pair[r] = hit != 0 ? __ffsll((unsigned long long)hit) - 1 : P;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t *__restrict__ ids, int P, int E, int bm, int32_t *__restrict__ sorted_ids,
     int32_t *__restrict__ tile_expert, int32_t *__restrict__ offsets,
@@ -330,8 +389,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     __shared__ AlignShared sh;
     if (P <= kWaveSortPairs) {
         if (threadIdx.x < 64)
-            align_wave(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
-                       bad_ids);
+            align_wave(sh.cnt, sh.off, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm,
+                       num_tiles, bad_ids);
         return;
     }
     align_block(sh, ids, P, E, bm, sorted_ids, tile_expert, offsets, inv_perm, num_tiles,
@@ -364,6 +423,97 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
         counts[(size_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
+// Device-coherent 4-byte store: the value is read by workgroups of the same
+// launch on other XCDs.
+__device__ __forceinline__ void store_coherent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// x in MFMA fragment order with minus its per-group bias term, for thread
+// `gid` of T * H / 8: GS / 8 consecutive threads per (token, group), 8
+// fragment positions each (one 16-byte store); the group's bias term is
+// summed across them with shuffles, so the threads of a group must run
+// together (whole groups per wave: GS / 8 divides 64).
+template <int BITS, int GS>
+__device__ __forceinline__ void prep_x(const uint16_t *__restrict__ x, const Workspace &ws, int T,
+                                       int H, int gid)
+{
+    constexpr int PL = GS / 8;
+    const int ngroups = H / GS;
+    const bool on = gid < T * ngroups * PL;
+    const int q = gid % PL, tg = gid / PL;
+    const int t = on ? tg / ngroups : 0, G = on ? tg % ngroups : 0;
+    const uint16_t *src = x + (size_t)t * H + (size_t)G * GS;
+    uint32_t e[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+        e[v] = on ? src[frag_src(BITS, GS, q * 8 + v)] : 0u;
+    float sum = 0.f;  // sum of (stored activation) * (its bias weight)
+    u32x4_t o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
+        const uint32_t lo = bf16_scaled(e[2 * h], frag_shift(BITS, GS, p0));
+        const uint32_t hi = bf16_scaled(e[2 * h + 1], frag_shift(BITS, GS, p1));
+        sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
+        sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
+        o[h] = lo | (hi << 16);
+    }
+#pragma unroll
+    for (int m = 1; m < PL; m <<= 1)
+        sum += __shfl_xor(sum, m, 64);
+    if (on) {
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS) + q;
+        float *bias = ws.x_bias + (size_t)t * ngroups + G;
+        *dst = o;
+        if (q == 0)
+            *bias = -sum;   // stored negated: the chain start
+    }
+}
+
+// The 8 consecutive fragment positions [8q, 8q + 8) of one group, from the
+// raw BF16 words `w` that frag_chunk_load fetched: position 8q + v holds the
+// group element that word half (v >> 1) + 4 (v & 1) carries (see frag_src),
+// divided by 2^frag_shift; `sum` gets their sum weighted by frag_bias_weight,
+// in the same order as prep_x.
+template <int BITS, int GS>
+__device__ __forceinline__ u32x4_t frag_chunk(const u32x4_t w, int q, float &sum)
+{
+    u32x4_t o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int p0 = q * 8 + 2 * h;   // p0 and p0 + 1 share shift and weight
+        const uint32_t lo0 = (w[h >> 1] >> (16 * (h & 1))) & 0xffffu;
+        const uint32_t hi0 = (w[2 + (h >> 1)] >> (16 * (h & 1))) & 0xffffu;
+        const uint32_t lo = bf16_scaled(lo0, frag_shift(BITS, GS, p0));
+        const uint32_t hi = bf16_scaled(hi0, frag_shift(BITS, GS, p0));
+        sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
+        sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p0);
+        o[h] = lo | (hi << 16);
+    }
+    return o;
+}
+
+// Raw words for frag_chunk: the group elements that positions [8q, 8q + 8)
+// hold, from the group's first element `grp` (16-byte aligned).  4-bit codes:
+// 8 consecutive elements from g * gs / 4 + 8 s; 2-bit codes: 4 consecutive
+// elements and the 4 that follow 8 later.
+template <int BITS, int GS>
+__device__ __forceinline__ u32x4_t frag_chunk_load(const uint16_t *grp, int q)
+{
+    const int pos = q * 8, st = pos >> 5, g = (pos >> 3) & 3;
+    if constexpr (BITS == 4) {
+        return *reinterpret_cast<const u32x4_t *>(grp + g * (GS / 4) + 8 * st);
+    } else {
+        const int base = GS == 32 ? 16 * (g >> 1) + 4 * (g & 1)
+                                  : g * (GS / 4) + 16 * (st >> 1) + 4 * (st & 1);
+        const u32x2_t a = *reinterpret_cast<const u32x2_t *>(grp + base);
+        const u32x2_t b = *reinterpret_cast<const u32x2_t *>(grp + base + 8);
+        return u32x4_t{a[0], a[1], b[0], b[1]};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Route kernel: blocks [0, nalign) sort the pairs; blocks [nalign, nalign +
 // nprep) reorder x into fragment order and compute minus c * (group sum) per
@@ -379,7 +529,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
     if (blk < nalign) {
         if (T * topk <= kWaveSortPairs) {
             if (threadIdx.x < 64)
-                align_wave(sh, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert,
+                align_wave(sh.cnt, sh.off, ids, T * topk, E, bm, ws.sorted_ids, ws.tile_expert,
                            ws.expert_offsets, ws.inv_perm, ws.meta, ws.meta + 1);
             return;
         }
@@ -389,39 +539,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_kernel(
         return;
     }
     if (blk < nalign + nprep) {
-        // GS / 8 consecutive threads per (token, group), 8 fragment
-        // positions each (one 16-byte store); the group's bias term is
-        // summed across them with shuffles
-        constexpr int PL = GS / 8;
-        const int ngroups = H / GS;
-        const int gid = (blk - nalign) * kAlignThreads + threadIdx.x;
-        const bool on = gid < T * ngroups * PL;   // whole groups: PL divides the block
-        const int q = gid % PL, tg = gid / PL;
-        const int t = on ? tg / ngroups : 0, G = on ? tg % ngroups : 0;
-        const uint16_t *src = x + (size_t)t * H + (size_t)G * GS;
-        uint32_t e[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-            e[v] = on ? src[frag_src(BITS, GS, q * 8 + v)] : 0u;
-        float sum = 0.f;  // sum of (stored activation) * (its bias weight)
-        u32x4_t o;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
-            const uint32_t lo = bf16_scaled(e[2 * h], frag_shift(BITS, GS, p0));
-            const uint32_t hi = bf16_scaled(e[2 * h + 1], frag_shift(BITS, GS, p1));
-            sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
-            sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
-            o[h] = lo | (hi << 16);
-        }
-#pragma unroll
-        for (int m = 1; m < PL; m <<= 1)
-            sum += __shfl_xor(sum, m, 64);
-        if (on) {
-            reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS)[q] = o;
-            if (q == 0)
-                ws.x_bias[(size_t)t * ngroups + G] = -sum;   // stored negated: the chain start
-        }
+        prep_x<BITS, GS>(x, ws, T, H, (blk - nalign) * kAlignThreads + threadIdx.x);
         return;
     }
     // zero the accumulator and the act bias terms (the decode epilogue adds into them)
@@ -467,6 +585,13 @@ struct GemmArgs {
     int32_t *tile_done;       // fused decode: w13 workgroups finished per tile, 16 ints apart
     int tile_target;          // fused decode w2: w13 workgroups per tile
     int32_t *status;          // fused decode w2: count of waits that gave up (meta word 2)
+    // single-launch decode
+    const int32_t *ids;       // routing ids: each workgroup looks its tile up
+    int E;
+    int nblk_self;            // workgroups of this GEMM per tile
+    int n_pre;                // prep workgroups
+    int32_t *prep_done;       // prep workgroups finished
+    int32_t *blocks_done;     // down-projection column blocks finished
     int K;                    // reduction length (H for w13, I for w2)
     int N;                    // output columns (I gate columns for w13, H for w2)
     int P, topk;
@@ -1183,7 +1308,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // holds, for each group of the unit, the dwords its MFMA fragments need
 // (dwords [g*n, g*n + n) of the group with n = gs*bits/128).
 // ---------------------------------------------------------------------------
-template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false, bool PREP = false>
+// ONE: the single-launch decode layer (FUSED too): the tile comes from the
+// routing ids; w13 stages x straight from the input rows in fragment order
+// (args.a is x) and stores each act group's bias term in halves (no zeroing
+// needed); w2 adds into the FP32 sum once this launch's prep workgroups have
+// zeroed it; the workgroup that finishes last resets every counter.
+template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false, bool PREP = false,
+          bool ONE = false>
 struct Stream {
     static constexpr int R = 4;                      // rows per tile
     static constexpr int NW = 4;                     // waves per workgroup
@@ -1354,10 +1485,15 @@ struct Stream {
         const int sr = r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3;
         const float *bp = args.a_bias + (size_t)(sr >= 0 ? sr : 0) * ngroups + G;
         float bv;
-        if constexpr (FUSED && !W13)   // written by this launch's w13 items
+        if constexpr (ONE && !W13) {   // the two halves the w13 items stored
+            const float *bq = args.a_bias + ((size_t)(sr >= 0 ? sr : 0) * ngroups + G) * 2;
+            bv = __hip_atomic_load(bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                 __hip_atomic_load(bq + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if constexpr (FUSED && !W13) {   // written by this launch's w13 items
             bv = __hip_atomic_load(bp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
+        } else {
             bv = *bp;
+        }
         return sr >= 0 ? bv : 0.f;
     }
 
@@ -1378,18 +1514,25 @@ struct Stream {
     static __device__ void run(const GemmArgs &args, int b, int nb)
     {
         extern __shared__ __align__(16) unsigned char smem[];
-        // the tile count, the tile's expert and its rows load together (one
-        // round trip; b < max_tiles keeps the last two in bounds, their
-        // values are unused past the last tile)
-        const int ntiles = *args.num_tiles;
-        const int e = args.tile_expert[b];
+        int ntiles, e;
         int pair[R];
+        if constexpr (ONE) {
+            // the same tile layout as the route kernel's sort, from the ids
+            wave_tile_lookup(args.ids, args.P, args.E, b, ntiles, e, pair);
+        } else {
+            // the tile count, the tile's expert and its rows load together
+            // (one round trip; b < max_tiles keeps the last two in bounds,
+            // their values are unused past the last tile)
+            ntiles = *args.num_tiles;
+            e = args.tile_expert[b];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            pair[r] = args.sorted_ids[b * R + r];
+            for (int r = 0; r < R; ++r)
+                pair[r] = args.sorted_ids[b * R + r];
+        }
         if (b >= ntiles) {
             // no tile at all (every id invalid): the output is the zeroed sum
-            if constexpr (!W13)
+            // (the single launch's prep writes it)
+            if constexpr (!W13 && !ONE)
                 if (args.out_bf16 && ntiles == 0 && b == 0)
                     convert_block(args, nb);
             return;
@@ -1436,6 +1579,14 @@ struct Stream {
                 brow[j] = args.codes + ((size_t)e * nrows + n) * kw;
         }
 
+        // ONE w2: whether the prep has zeroed the FP32 sum, loaded early (its
+        // latency hides behind the wait for the tile's w13 items)
+        int prep_seen = 0;
+        if constexpr (ONE && !W13)
+            if (tid == 0)
+                prep_seen = __hip_atomic_load(args.prep_done, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+
         // The weight stream starts first: its HBM latency overlaps the staging.
         uint32_t q[D][NB][UDW];
 #pragma unroll
@@ -1446,13 +1597,24 @@ struct Stream {
             // the tile's act rows and bias terms come from this launch's w13
             // items: wait (bounded) until all of them are done
             if (tid == 0) {
-                const int32_t *cnt = args.tile_done + b * 16;
+                int32_t *cnt = args.tile_done + b * 16;
                 bool ready = false;
                 for (int it = 0; it < (1 << 22) && !ready; ++it) {
-                    ready = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                            args.tile_target;
+                    const int v =
+                        __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ready = v >= args.tile_target;
                     if (!ready)
                         __builtin_amdgcn_s_sleep(2);
+                }
+                if constexpr (ONE) {
+                    // the FP32 sum this workgroup adds into must be zeroed
+                    bool zeroed = prep_seen >= args.n_pre;
+                    for (int it = 0; it < (1 << 22) && !zeroed; ++it) {
+                        __builtin_amdgcn_s_sleep(2);
+                        zeroed = __hip_atomic_load(args.prep_done, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) >= args.n_pre;
+                    }
+                    ready = ready && zeroed;
                 }
                 // a wait that reached its bound is counted where the host can
                 // read it: the act rows staged below may then be incomplete
@@ -1466,13 +1628,18 @@ struct Stream {
         // Activation rows (zero for padding rows), their bias terms and this
         // workgroup's scales go to LDS.  Each pass issues all of its loads
         // before its first LDS store, so the latencies overlap; the first bias
-        // items load together with the first pass.
+        // items load together with the first pass.  XDIRECT (single-launch
+        // w13): the rows are x itself, put in fragment order here, and the
+        // group bias terms are summed here (GS / 8 consecutive lanes hold one
+        // group's chunks).
+        constexpr bool XDIRECT = ONE && W13;
         float bpre[NBIAS_PRE];
 #pragma unroll
         for (int k = 0; k < NBIAS_PRE; ++k) {
             const int i = tid + k * NTHREADS;
-            bpre[k] = i < R * ngroups ? bias_item(args, src[0], src[1], src[2], src[3], i, ngroups)
-                                          : 0.f;
+            bpre[k] = !XDIRECT && i < R * ngroups
+                          ? bias_item(args, src[0], src[1], src[2], src[3], i, ngroups)
+                          : 0.f;
         }
         {
             const int k8n = K / 8;
@@ -1480,16 +1647,24 @@ struct Stream {
             const bool svec = ngroups % 8 == 0 && reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
             const int sper = ngroups / 8;                  // 16-byte scale pieces per row
             const int spieces = svec ? srows * sper : 0;
-            for (int k0 = 0; k0 < k8n || k0 < spieces; k0 += 2 * NTHREADS) {
-                u32x4_t v[2][R], vs[2];
+            // chunks per thread and pass (one with XDIRECT: fewer live registers)
+            constexpr int TP = XDIRECT ? 1 : 2;
+            for (int k0 = 0; k0 < k8n || k0 < spieces; k0 += TP * NTHREADS) {
+                u32x4_t v[TP][R], vs[TP];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TP; ++t) {
                     const int k8 = k0 + t * NTHREADS + tid;
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         v[t][r] = u32x4_t{0u, 0u, 0u, 0u};
-                        if (src[r] >= 0 && k8 < k8n)
-                            v[t][r] = load_a(args.a + (size_t)src[r] * K + (size_t)k8 * 8);
+                        if (src[r] >= 0 && k8 < k8n) {
+                            if constexpr (XDIRECT)
+                                v[t][r] = frag_chunk_load<BITS, GS>(
+                                    args.a + (size_t)src[r] * K + (size_t)(k8 / (GS / 8)) * GS,
+                                    k8 % (GS / 8));
+                            else
+                                v[t][r] = load_a(args.a + (size_t)src[r] * K + (size_t)k8 * 8);
+                        }
                     }
                     vs[t] = u32x4_t{0u, 0u, 0u, 0u};
                     if (k8 < spieces) {
@@ -1506,8 +1681,22 @@ struct Stream {
                     }
                 }
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TP; ++t) {
                     const int k8 = k0 + t * NTHREADS + tid;
+                    if constexpr (XDIRECT) {
+                        // k8 < k8n is the same for the GS / 8 lanes of a group
+                        constexpr int PL = GS / 8;
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float sum = 0.f;
+                            v[t][r] = frag_chunk<BITS, GS>(v[t][r], k8 % PL, sum);
+#pragma unroll
+                            for (int m = 1; m < PL; m <<= 1)
+                                sum += __shfl_xor(sum, m, 64);
+                            if (k8 < k8n && k8 % PL == 0)   // stored negated: the chain start
+                                sBias[(k8 / PL) * R + r] = src[r] >= 0 ? -sum : 0.f;
+                        }
+                    }
                     if (k8 < k8n) {
 #pragma unroll
                         for (int r = 0; r < R; ++r)
@@ -1520,15 +1709,17 @@ struct Stream {
                             vs[t];
                 }
             }
-            for (int i = tid; i < R * ngroups; i += NTHREADS) {
-                if (i < NBIAS_PRE * NTHREADS)
-                    continue;   // staged from the batch loaded above
-                sBias[i] = bias_item(args, src[0], src[1], src[2], src[3], i, ngroups);
-            }
+            if constexpr (!XDIRECT) {
+                for (int i = tid; i < R * ngroups; i += NTHREADS) {
+                    if (i < NBIAS_PRE * NTHREADS)
+                        continue;   // staged from the batch loaded above
+                    sBias[i] = bias_item(args, src[0], src[1], src[2], src[3], i, ngroups);
+                }
 #pragma unroll
-            for (int k = 0; k < NBIAS_PRE; ++k)
-                if (tid + k * NTHREADS < R * ngroups)
-                    sBias[tid + k * NTHREADS] = bpre[k];
+                for (int k = 0; k < NBIAS_PRE; ++k)
+                    if (tid + k * NTHREADS < R * ngroups)
+                        sBias[tid + k * NTHREADS] = bpre[k];
+            }
             if (!svec) {   // scales without 16-byte alignment: one half at a time
                 for (int i = tid; i < srows * ngroups; i += NTHREADS) {
                     const int rr = i / ngroups, G = i % ngroups;
@@ -1621,7 +1812,17 @@ struct Stream {
                 for (int t = 0; t < gspan; ++t)
                     sum += s_part[v][k * gspan + t];
                 const int G2 = (nb * BN + k * gspan * 16) / gs2;
-                unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2, -sum);
+                if constexpr (ONE) {
+                    // a group is at most two workgroups wide: each stores its half,
+                    // a group inside one workgroup stores a zero second half
+                    float *dst = args.act_bias_out + ((size_t)(b * R + v) * ngroups2 + G2) * 2;
+                    store_coherent(dst + (gs2 > BN ? nb % 2 : 0), -sum);
+                    if (gs2 <= BN)
+                        store_coherent(dst + 1, 0.f);
+                } else {
+                    unsafeAtomicAdd(args.act_bias_out + (size_t)(b * R + v) * ngroups2 + G2,
+                                    -sum);
+                }
             }
             if constexpr (FUSED) {
                 // act and its bias terms are performed (device scope): count
@@ -1649,19 +1850,44 @@ struct Stream {
     // Small outputs: every workgroup counts itself done in its column block
     // once its atomics have been performed (each wave waits for them); the
     // last one of the block rounds the block's columns of every token,
-    // reading them with device-coherent loads.  No cache flush is needed: the
-    // accumulator only ever changes through device-scope atomics.
+    // reading them with device-coherent loads, and clears the block's
+    // counter.  No cache flush is needed: the accumulator only ever changes
+    // through device-scope atomics.  In the single launch the last block to
+    // finish comes after every other workgroup has passed its waits: it
+    // clears the prep and per-tile counters for the next call.
     static __device__ void arrive(const GemmArgs &args, int active, int nb)
     {
-        __shared__ int last;
+        __shared__ int last, fin;
+        const int tid = threadIdx.x;
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's atomics are done
         __syncthreads();
-        if (threadIdx.x == 0)
+        if (tid == 0)
             last = __hip_atomic_fetch_add(args.done + nb * 16, 1, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT) == active - 1;
         __syncthreads();
-        if (last)
-            convert_block(args, nb);
+        if (!last)
+            return;
+        if constexpr (ONE)
+            if (tid == 0)
+                fin = __hip_atomic_fetch_add(args.blocks_done, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == args.nblk_self - 1;
+        convert_block(args, nb);
+        if (tid == 0)
+            __hip_atomic_store(args.done + nb * 16, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (ONE) {
+            __syncthreads();
+            if (fin) {
+                for (int i = tid; i < active; i += NTHREADS)
+                    __hip_atomic_store(args.tile_done + i * 16, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (tid == 0) {
+                    __hip_atomic_store(args.prep_done, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(args.blocks_done, 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
     }
     static __device__ void convert_block(const GemmArgs &args, int nb)
     {
@@ -1712,6 +1938,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     else
         Stream<B2, G2, 2, D2, false, true, PREP>::run(a2, (id - n13) / nblk2,
                                                       (id - n13) % nblk2);
+}
+
+// The single-launch decode's first n_pre workgroups (256 threads each):
+// they zero the FP32 sum with device-coherent stores and count themselves
+// done (the w2 items add into the sum only after that); then the first one's
+// first wave sorts the pairs into the workspace (results the host may read;
+// the GEMM items look their tiles up from the ids).  With no tile at all no
+// GEMM item runs: the last prep workgroup writes the zero output and clears
+// the counter itself.
+__device__ void decode_prep(const GemmArgs &a13, const GemmArgs &a2, const Workspace &ws, int T,
+                            int H, int wg)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_last, s_ntiles;
+    const int tid = threadIdx.x;
+    const int nthr = a13.n_pre * 256, gid = wg * 256 + tid;
+    uint64_t *o = reinterpret_cast<uint64_t *>(ws.out_f32);
+    for (int i = gid; i < T * H / 2; i += nthr)
+        __hip_atomic_store(o + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stores are performed
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(a13.prep_done, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == a13.n_pre - 1;
+    if (wg == 0 && tid < 64) {
+        if (tid == 0)   // waits that gave up: counted afresh by every call
+            __hip_atomic_store(a2.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int *cnt = reinterpret_cast<int *>(smem);
+        align_wave(cnt, cnt + a13.E, a13.ids, a13.P, a13.E, kDecodeRows, ws.sorted_ids,
+                   ws.tile_expert, ws.expert_offsets, ws.inv_perm, ws.meta, ws.meta + 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    if (tid < 64) {
+        int nt, e, pair[kDecodeRows];
+        wave_tile_lookup(a13.ids, a13.P, a13.E, 0, nt, e, pair);
+        if (tid == 0)
+            s_ntiles = nt;
+    }
+    __syncthreads();
+    if (s_ntiles != 0)
+        return;
+    for (int i = tid; i < T * H; i += 256)
+        a2.out_bf16[i] = 0;
+    if (tid == 0)
+        __hip_atomic_store(a13.prep_done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The whole decode-shaped layer in one launch: workgroups [0, n_pre) are the
+// prep (decode_prep), then the w13 (tile, column block) items, tile-major,
+// then the w2 items.  Workgroups are dispatched in id order, so every item a
+// workgroup waits for has been dispatched before it.
+template <int BITS, int GS, int D13, int D2, bool PREP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_layer_kernel(
+    const GemmArgs a13, const GemmArgs a2, const Workspace ws, int T, int H, int max_tiles,
+    int nblk13, int nblk2)
+{
+    const int id = (int)blockIdx.x - a13.n_pre, n13 = max_tiles * nblk13;
+    if (id < 0)
+        decode_prep(a13, a2, ws, T, H, (int)blockIdx.x);
+    else if (id < n13)
+        Stream<BITS, GS, 2, D13, true, true, PREP, true>::run(a13, id / nblk13, id % nblk13);
+    else
+        Stream<BITS, GS, 2, D2, false, true, PREP, true>::run(a2, (id - n13) / nblk2,
+                                                              (id - n13) % nblk2);
 }
 
 __global__ void convert_kernel(const float *__restrict__ src, uint16_t *__restrict__ dst,
@@ -2115,6 +2407,71 @@ hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t 
     case 4032: return decode_dispatch<4, 32>(a13, a2, d.max_tiles, stream, ev);
     case 4064: return decode_dispatch<4, 64>(a13, a2, d.max_tiles, stream, ev);
     case 4128: return decode_dispatch<4, 128>(a13, a2, d.max_tiles, stream, ev);
+    default: return hipErrorNotSupported;
+    }
+}
+
+template <int BITS, int GS>
+static hipError_t decode_layer_dispatch(const uint16_t *x, const int32_t *ids, GemmArgs a13,
+                                        GemmArgs a2, const LayerDims &d, const Workspace &ws,
+                                        hipStream_t stream, const KernelEvents &ev)
+{
+    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
+    using S13 = Stream<BITS, GS, 2, D13, true, true, false, true>;
+    using S2 = Stream<BITS, GS, 2, D2, false, true, false, true>;
+    const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
+    const long prep_threads = (long)d.T * d.H / 8;   // 4 zeroing stores each
+    const int n_pre = (int)((prep_threads + 255) / 256);
+    if (d.T * d.topk > kSingleLaunchPairs || d.max_tiles > kSyncTiles || nblk2 > kSyncBlocks ||
+        d.block_m != kDecodeRows || n_pre < 1)
+        return hipErrorInvalidValue;
+    for (GemmArgs *a : {&a13, &a2}) {
+        a->ids = ids;
+        a->E = d.E;
+        a->n_pre = n_pre;
+        a->prep_done = ws.prep_done;
+        a->blocks_done = ws.blocks_done;
+        a->tile_done = ws.sync_tiles;
+        a->status = ws.meta + 2;
+    }
+    a13.a = x;   // staged straight from the input rows
+    a13.nblk_self = nblk13;
+    a2.nblk_self = nblk2;
+    a2.tile_target = nblk13;
+    a2.done = ws.sync_done;
+    size_t lds = S13::lds_bytes(a13.K);
+    if (S2::lds_bytes(a2.K) > lds)
+        lds = S2::lds_bytes(a2.K);
+    if ((size_t)2 * d.E * sizeof(int) > lds)   // the sort's per-expert counts and offsets
+        lds = (size_t)2 * d.E * sizeof(int);
+    const dim3 grid((unsigned)(n_pre + d.max_tiles * (nblk13 + nblk2)));
+    if (a13.prepared)
+        hipExtLaunchKernelGGL((decode_layer_kernel<BITS, GS, D13, D2, true>), grid, dim3(256),
+                              (uint32_t)lds, stream, ev.start, ev.stop, 0, a13, a2, ws, d.T,
+                              d.H, d.max_tiles, nblk13, nblk2);
+    else
+        hipExtLaunchKernelGGL((decode_layer_kernel<BITS, GS, D13, D2, false>), grid, dim3(256),
+                              (uint32_t)lds, stream, ev.start, ev.stop, 0, a13, a2, ws, d.T,
+                              d.H, d.max_tiles, nblk13, nblk2);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_layer(const uint16_t *x, const int32_t *topk_ids, const int32_t *w13,
+                               const uint16_t *s13, const int32_t *w2, const uint16_t *s2,
+                               const float *topk_w, const LayerDims &d, const Workspace &ws,
+                               hipStream_t stream, const KernelEvents &ev, uint16_t *out_bf16)
+{
+    if (d.variant13 != 2 || d.variant2 != 2 || !out_bf16 ||
+        !decode_one_launch(d.bits13, d.g13, d.bits2, d.g2, d.H, d.I))
+        return hipErrorNotSupported;
+    const GemmArgs a13 = w13_args(w13, s13, d, ws);
+    const GemmArgs a2 = w2_args(w2, s2, topk_w, d, ws, out_bf16);
+    switch (d.bits13 * 1000 + d.g13) {
+    case 2064: return decode_layer_dispatch<2, 64>(x, topk_ids, a13, a2, d, ws, stream, ev);
+    case 2128: return decode_layer_dispatch<2, 128>(x, topk_ids, a13, a2, d, ws, stream, ev);
+    case 4032: return decode_layer_dispatch<4, 32>(x, topk_ids, a13, a2, d, ws, stream, ev);
+    case 4064: return decode_layer_dispatch<4, 64>(x, topk_ids, a13, a2, d, ws, stream, ev);
+    case 4128: return decode_layer_dispatch<4, 128>(x, topk_ids, a13, a2, d, ws, stream, ev);
     default: return hipErrorNotSupported;
     }
 }

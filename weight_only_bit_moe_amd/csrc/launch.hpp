@@ -24,7 +24,21 @@ struct Workspace {
     int32_t *done;            // [H / 64][16]: decode w2 workgroups finished per column block
     int32_t *tile_done;       // [max_tiles][16]: fused decode, w13 workgroups finished per tile
     int32_t *xcd_first;       // [2][kSplitEntries]: tile kernel item range per XCD, w13 then w2
+    // Single-launch decode: counters in the fixed region at the start of the
+    // workspace, zero between calls (the call's last workgroup resets them).
+    int32_t *prep_done;       // prep workgroups finished
+    int32_t *blocks_done;     // down-projection column blocks finished
+    int32_t *sync_tiles;      // [kSyncTiles][16]: gate/up workgroups finished per tile
+    int32_t *sync_done;       // [kSyncBlocks][16]: down workgroups finished per column block
 };
+
+// Fixed region at the start of every workspace (byte offsets): the status
+// words, then the single-launch decode counters, each on its own 64 bytes.
+constexpr size_t kSyncBytes = 32768;
+constexpr size_t kSyncPrepDone = 256, kSyncBlocksDone = 320, kSyncTilesAt = 1024;
+constexpr int kSyncTiles = 128, kSyncBlocks = 128;
+constexpr size_t kSyncDoneAt = kSyncTilesAt + (size_t)kSyncTiles * 64;
+static_assert(kSyncDoneAt + (size_t)kSyncBlocks * 64 <= kSyncBytes, "sync region");
 
 // Entries per GEMM of the tile kernel's XCD split: 8 range starts and the total.
 constexpr int kSplitEntries = 9;
@@ -87,6 +101,17 @@ hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t 
                          uint16_t *out_bf16);
 // Whether decode-shaped w13 and w2 of these formats and sizes run as one launch.
 bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I);
+// The whole decode-shaped layer in one launch (routing, activation reorder,
+// zeroing, both GEMMs and the rounding): workgroups [0, n_pre) do the
+// routing's work, the rest are the shared-launch GEMM items.  Needs the
+// one-launch GEMMs, the fused rounding, at most 64 pairs, max_tiles <=
+// kSyncTiles and H / 128 <= kSyncBlocks.
+hipError_t launch_decode_layer(const uint16_t *x, const int32_t *topk_ids, const int32_t *w13,
+                               const uint16_t *s13, const int32_t *w2, const uint16_t *s2,
+                               const float *topk_w, const LayerDims &d, const Workspace &ws,
+                               hipStream_t stream, const KernelEvents &ev, uint16_t *out_bf16);
+// Pairs up to which the single-launch decode's tile lookup works (one wave).
+constexpr int kSingleLaunchPairs = 64;
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
