@@ -402,6 +402,8 @@ def measure_layer(cfg, args, steps, warmup, codes, spec=None):
         "gpu_ms_per_step_events": float(np.mean(step_gpu_ms)),
         "algorithmic_bytes": layer_bytes,
         "algorithmic_flops": layer_flops,
+        "kernel_algorithmic_bytes": {n: alg_bytes[n] for n in avg if n in alg_bytes},
+        "kernel_algorithmic_flops": {n: alg_flops[n] for n in avg if n in alg_flops},
         "implementation_bytes": impl_bytes,
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
         "layer_hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
