@@ -99,6 +99,9 @@ typedef struct {
                             /*    rounding) is one launch: gemms_one_launch and     */
                             /*    convert_in_w2 with T*topk <= 64, max_tiles <= 128 */
                             /*    and H <= 16384                                    */
+    int32_t w13_ksplit;     /* single launch: K slices per gate/up (tile, column    */
+                            /*    block), each its own workgroup (1, 2 or 4; more   */
+                            /*    when few tiles would leave the GPU idle)          */
 } moe_wna16_plan_t;
 
 /*

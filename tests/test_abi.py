@@ -86,6 +86,17 @@ def test_plan_reports_shared_launches(lib):
     assert over["gemms_one_launch"] == 1 and over["single_launch"] == 0   # 65 pairs
     for p in (mixed, g32, pre, big_t):
         assert p["single_launch"] == 0
+    # a small intermediate (one GPU's share under tensor parallelism 4) runs the
+    # shared launches with half the w2 prefetch depth, and the single launch
+    # splits each gate/up item's K in 4 (192 items would leave the GPU idle)
+    tp4 = M.moe_wna16_plan(4, 4096, 512, 256, 6, (2, 128), (2, 128))
+    assert tp4["gemms_one_launch"] == 1 and tp4["single_launch"] == 1
+    assert tp4["w13_ksplit"] == 4
+    assert dec["w13_ksplit"] == 1                            # 768 items already
+    tp4_4b = M.moe_wna16_plan(4, 4096, 512, 256, 6, (4, 128), (4, 128))
+    assert tp4_4b["single_launch"] == 1 and tp4_4b["w13_ksplit"] == 4
+    for p in (bdec, pre, mixed):
+        assert p["w13_ksplit"] == 1
 
 
 NAN, INF = float("nan"), math.inf

@@ -396,6 +396,45 @@ def test_decode_w2g128_i2048(dev, T, prepared):
     G.assert_parity(got, O.forward_layer(L), "2-bit g128, I=2048")
 
 
+@pytest.mark.parametrize("q,H,ksplit", [((2, 128), 4096, 4), ((2, 64), 4096, 4),
+                                        ((4, 32), 2048, 4), ((4, 64), 4096, 4),
+                                        ((4, 128), 4096, 4), ((2, 128), 2048, 2)])
+def test_single_launch_split_gate_up(dev, q, H, ksplit):
+    """Few tiles in the single launch (I = 512, one GPU's share under tensor
+    parallelism 4): each gate/up (tile, column block) runs as `ksplit` K-slice
+    workgroups whose partial sums the last one completes; plain, partly
+    invalid ids, and prepared codes, on one workspace (run_layer also checks
+    the counters are clear after each call)."""
+    sp = spec(T=4, H=H, I=512, E=64, topk=6, bits13=q[0], group13=q[1], bits2=q[0],
+              group2=q[1], **ACT)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, q, q)
+    assert plan["single_launch"] == 1 and plan["w13_ksplit"] == ksplit
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    for seed, kind, prepared in ((120, "plain", False), (121, "bad", False),
+                                 (122, "plain", True)):
+        L = make_layer(sp, seed=seed)
+        if kind == "bad":
+            L.topk_ids[1, :3] = -1
+            L.topk_ids[2, 0] = sp.E
+        _, got = G.run_layer(L, dev, workspace=ws, prepared=prepared)
+        G.assert_parity(got, O.forward_layer(L), f"split gate/up, {kind}")
+
+
+@pytest.mark.parametrize("q", [(2, 128), (4, 128), (4, 64)])
+def test_shared_launch_small_intermediate(dev, q):
+    """96 pairs at I = 512: the shared w13 + w2 launch (not the single one)
+    with the w2 prefetch depth that I allows (half the usual for 2- and
+    4-bit group-128 codes), checkpoint and prepared codes."""
+    sp = spec(T=16, H=1024, I=512, E=32, topk=6, bits13=q[0], group13=q[1], bits2=q[0],
+              group2=q[1], **ACT)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, q, q)
+    assert plan["gemms_one_launch"] == 1 and plan["single_launch"] == 0
+    for prepared in (False, True):
+        L = make_layer(sp, seed=130 + int(prepared))
+        _, got = G.run_layer(L, dev, prepared=prepared)
+        G.assert_parity(got, O.forward_layer(L), "shared launch, I = 512")
+
+
 # --------------------------------------------------------------------------
 # full-size workloads, sampled tokens
 # --------------------------------------------------------------------------

@@ -33,7 +33,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
                 ("w13_variant", ctypes.c_int32), ("w2_variant", ctypes.c_int32),
                 ("gemms_one_launch", ctypes.c_int32), ("convert_in_w2", ctypes.c_int32),
-                ("single_launch", ctypes.c_int32)]
+                ("single_launch", ctypes.c_int32), ("w13_ksplit", ctypes.c_int32)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -165,7 +165,8 @@ def moe_wna16_plan(T, H, I, E, topk, q13: Tuple[int, int], q2: Tuple[int, int]) 
         raise MoeWna16Error(st, "moe_wna16_plan")
     return dict(block_m=plan.block_m, max_tiles=plan.max_tiles, w13_variant=plan.w13_variant,
                 w2_variant=plan.w2_variant, gemms_one_launch=plan.gemms_one_launch,
-                convert_in_w2=plan.convert_in_w2, single_launch=plan.single_launch)
+                convert_in_w2=plan.convert_in_w2, single_launch=plan.single_launch,
+                w13_ksplit=plan.w13_ksplit)
 
 
 def moe_wna16_forward(x, topk_ids, topk_w, w13_packed, w13_scales, w2_packed, w2_scales, T, H,

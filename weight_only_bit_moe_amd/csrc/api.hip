@@ -48,7 +48,7 @@ int check_sizes(int T, int H, int I, int E, int topk)
 
 struct Layout {
     size_t meta, offsets, sorted, tiles, inv, xperm, xbias, act, actbias, outf32, ccounts, done,
-        tdone, total;
+        tdone, hsum, total;
 };
 
 // Workspace pieces for tiles of at most `bm` rows (the sort's padded slots
@@ -83,6 +83,9 @@ Layout layout_for(int T, int H, int I, int E, int topk, int bm)
     L.ccounts = take((size_t)wna16::align_chunks((long long)P) * (E + 1) * sizeof(int32_t));
     L.done = take((size_t)H);   // one counter per 64 output columns, 64 bytes apart
     L.tdone = take(max_tiles * 64);   // one counter per tile, 64 bytes apart
+    // single-launch decode (at most 64 pairs): the split w13 items' FP32
+    // pre-activation sums, 2I per 4-row tile row (at most P + 3 min(E, P) rows)
+    L.hsum = take(P <= (size_t)wna16::kSingleLaunchPairs ? (P + 3 * minEP) * 2 * (size_t)I * 4 : 0);
     L.total = o;
     return L;
 }
@@ -124,6 +127,9 @@ void make_plan(int T, int H, int I, int E, int topk, moe_wna16_qparams q13,
                                   H / 128 <= wna16::kSyncBlocks
                               ? 1
                               : 0;
+    plan->w13_ksplit = plan->single_launch
+                           ? wna16::decode_layer_ksplit(q13.bits, q13.group, H, I, plan->max_tiles)
+                           : 1;
 }
 
 // The prefill-shaped kernels address activations, their bias terms and one
@@ -343,11 +349,15 @@ static int forward_impl(const void *x, const int32_t *topk_ids, const float *top
     ws.chunk_counts = reinterpret_cast<int32_t *>(base + L.ccounts);
     ws.done = reinterpret_cast<int32_t *>(base + L.done);
     ws.tile_done = reinterpret_cast<int32_t *>(base + L.tdone);
+    ws.hsum = (long long)T * topk <= wna16::kSingleLaunchPairs
+                  ? reinterpret_cast<float *>(base + L.hsum)
+                  : nullptr;
     ws.xcd_first = ws.meta + 8;
     ws.prep_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncPrepDone);
     ws.blocks_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncBlocksDone);
     ws.sync_tiles = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncTilesAt);
     ws.sync_done = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncDoneAt);
+    ws.sync_split = reinterpret_cast<int32_t *>(base + L.meta + wna16::kSyncSplitAt);
 
     wna16::KernelEvents ev[4];
     if (events)

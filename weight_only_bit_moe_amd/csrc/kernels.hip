@@ -592,6 +592,9 @@ struct GemmArgs {
     int n_pre;                // prep workgroups
     int32_t *prep_done;       // prep workgroups finished
     int32_t *blocks_done;     // down-projection column blocks finished
+    int ksplit;               // w13: K slices per (tile, column block), each its own workgroup
+    float *hsum;              // w13 with ksplit > 1: [tile rows][2N] FP32 pre-activations
+    int32_t *split_done;      // w13 with ksplit > 1: slices finished per (tile, column block)
     int K;                    // reduction length (H for w13, I for w2)
     int N;                    // output columns (I gate columns for w13, H for w2)
     int P, topk;
@@ -1312,7 +1315,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // routing ids; w13 stages x straight from the input rows in fragment order
 // (args.a is x) and stores each act group's bias term in halves (no zeroing
 // needed); w2 adds into the FP32 sum once this launch's prep workgroups have
-// zeroed it; the workgroup that finishes last resets every counter.
+// zeroed it; the workgroup that finishes last resets every counter.  With
+// args.ksplit > 1 a w13 (tile, column block) runs as that many workgroups,
+// each over one K slice: they add their partial pre-activations into
+// args.hsum (zeroed by the prep) and the last one of them runs the epilogue.
 template <int BITS, int GS, int NB, int D, bool W13, bool FUSED = false, bool PREP = false,
           bool ONE = false>
 struct Stream {
@@ -1511,7 +1517,7 @@ struct Stream {
         }
     }
 
-    static __device__ void run(const GemmArgs &args, int b, int nb)
+    static __device__ void run(const GemmArgs &args, int b, int nb, int ks = 0)
     {
         extern __shared__ __align__(16) unsigned char smem[];
         int ntiles, e;
@@ -1537,8 +1543,12 @@ struct Stream {
                     convert_block(args, nb);
             return;
         }
-        const int K = args.K;
-        const int ngroups = K / GS;
+        // this workgroup's K slice (the whole row unless a w13 item is split)
+        const int nsplit = (ONE && W13) ? args.ksplit : 1;
+        const int K = args.K / nsplit;                 // slice length
+        const int kofs = ks * K;                       // slice start
+        const int ngroups = K / GS;                    // groups of the slice (LDS layout)
+        const int ngroups_row = args.K / GS;           // groups of a whole row (HBM strides)
         const int lds_stride = K + 8;
         // LDS: R activation rows + a zero row; the rows' negated bias terms as
         // [group][row]; the workgroup's scales
@@ -1562,8 +1572,10 @@ struct Stream {
 
         // this lane's weight rows
         const int nrows = W13 ? 2 * args.N : args.N;
-        const int kw = K * BITS / 32;
-        const int nunits = K / UK;   // K % UK == 0: the plan sends other K to tile_kernel
+        const int kw = args.K * BITS / 32;
+        const int nunits_row = args.K / UK;   // K % UK == 0: the plan sends other K to tile_kernel
+        const int nunits = K / UK;            // units of the slice
+        const int ubase = ks * nunits;        // its first unit
         const uint32_t *brow[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -1572,18 +1584,20 @@ struct Stream {
                 n = nb * BN + wave * COLS + (j % (NB / 2)) * 16 + c + (j >= NB / 2 ? args.N : 0);
             else
                 n = nb * BN + wave * COLS + j * 16 + c;
-            if constexpr (PREP)   // block (row / 16, unit 0), this lane's slot
-                brow[j] = args.codes + ((size_t)e * (nrows / 16) + n / 16) * nunits * kPrepBlockDwords +
+            if constexpr (PREP)   // block (row / 16, first unit of the slice), this lane's slot
+                brow[j] = args.codes +
+                          (((size_t)e * (nrows / 16) + n / 16) * nunits_row + ubase) * kPrepBlockDwords +
                           prep_block_dword(BITS, GS, g, c, 0);
             else
-                brow[j] = args.codes + ((size_t)e * nrows + n) * kw;
+                brow[j] = args.codes + ((size_t)e * nrows + n) * kw + (size_t)ubase * 16;
         }
 
-        // ONE w2: whether the prep has zeroed the FP32 sum, loaded early (its
-        // latency hides behind the wait for the tile's w13 items)
+        // ONE w2 (and split w13): whether the prep has zeroed the FP32 sums
+        // this workgroup adds into, loaded early (its latency hides behind
+        // the weight stream or the wait for the tile's w13 items)
         int prep_seen = 0;
-        if constexpr (ONE && !W13)
-            if (tid == 0)
+        if constexpr (ONE)
+            if (tid == 0 && (!W13 || nsplit > 1))
                 prep_seen = __hip_atomic_load(args.prep_done, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
 
@@ -1644,7 +1658,8 @@ struct Stream {
         {
             const int k8n = K / 8;
             const int srows = NW * NB * 16;
-            const bool svec = ngroups % 8 == 0 && reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
+            const bool svec = ngroups % 8 == 0 && ngroups_row % 8 == 0 &&
+                              reinterpret_cast<uintptr_t>(args.scales) % 16 == 0;
             const int sper = ngroups / 8;                  // 16-byte scale pieces per row
             const int spieces = svec ? srows * sper : 0;
             // chunks per thread and pass (one with XDIRECT: fewer live registers)
@@ -1660,10 +1675,12 @@ struct Stream {
                         if (src[r] >= 0 && k8 < k8n) {
                             if constexpr (XDIRECT)
                                 v[t][r] = frag_chunk_load<BITS, GS>(
-                                    args.a + (size_t)src[r] * K + (size_t)(k8 / (GS / 8)) * GS,
+                                    args.a + (size_t)src[r] * args.K + kofs +
+                                        (size_t)(k8 / (GS / 8)) * GS,
                                     k8 % (GS / 8));
                             else
-                                v[t][r] = load_a(args.a + (size_t)src[r] * K + (size_t)k8 * 8);
+                                v[t][r] = load_a(args.a + (size_t)src[r] * args.K + kofs +
+                                                 (size_t)k8 * 8);
                         }
                     }
                     vs[t] = u32x4_t{0u, 0u, 0u, 0u};
@@ -1677,7 +1694,8 @@ struct Stream {
                         else
                             n = nb * BN + w * COLS + j * 16 + cc;
                         vs[t] = *reinterpret_cast<const u32x4_t *>(
-                            args.scales + ((size_t)e * nrows + n) * ngroups + kk * 8);
+                            args.scales + ((size_t)e * nrows + n) * ngroups_row + kofs / GS +
+                            kk * 8);
                     }
                 }
 #pragma unroll
@@ -1730,7 +1748,7 @@ struct Stream {
                             (j >= NB / 2 ? args.N : 0);
                     else
                         n = nb * BN + w * COLS + j * 16 + cc;
-                    sS[i] = args.scales[((size_t)e * nrows + n) * ngroups + G];
+                    sS[i] = args.scales[((size_t)e * nrows + n) * ngroups_row + kofs / GS + G];
                 }
             }
         }
@@ -1769,6 +1787,56 @@ struct Stream {
 
         // tile row g of every subtile lives in lane group g, element 0
         static_assert(R == 4, "one tile row per lane group");
+        if constexpr (ONE && W13) {
+            if (nsplit > 1) {
+                // The sums this slice adds into must have been zeroed by the
+                // prep (bounded wait; a give-up is counted).
+                __shared__ int s_last_split;
+                if (tid == 0) {
+                    bool zeroed = prep_seen >= args.n_pre;
+                    for (int it = 0; it < (1 << 22) && !zeroed; ++it) {
+                        __builtin_amdgcn_s_sleep(2);
+                        zeroed = __hip_atomic_load(args.prep_done, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) >= args.n_pre;
+                    }
+                    if (!zeroed)
+                        __hip_atomic_fetch_add(args.status, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+                // this slice's partial pre-activations (gate and up columns)
+                float *hrow = args.hsum + (size_t)(b * R + g) * 2 * args.N;
+                if (g < rows_real) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        unsafeAtomicAdd(hrow + nb * BN + wave * COLS + (j % (NB / 2)) * 16 + c +
+                                            (j >= NB / 2 ? args.N : 0),
+                                        acc[j][0]);
+                }
+                // the last slice of (tile, column block) to finish runs the
+                // epilogue on the complete sums and clears the slice counter
+                __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's atomics are done
+                __syncthreads();
+                if (tid == 0) {
+                    int32_t *cnt = args.split_done + b * args.nblk_self + nb;
+                    s_last_split = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+                    if (s_last_split)
+                        __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+                if (!s_last_split)
+                    return;
+                if (g < rows_real) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[j][0] = __hip_atomic_load(
+                            hrow + nb * BN + wave * COLS + (j % (NB / 2)) * 16 + c +
+                                (j >= NB / 2 ? args.N : 0),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
         if constexpr (W13) {
             constexpr int NG = NB / 2;
             const int gs2 = args.gs_next, bits2 = args.bits_next;
@@ -1941,14 +2009,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 }
 
 // The single-launch decode's first n_pre workgroups (256 threads each):
-// they zero the FP32 sum with device-coherent stores and count themselves
-// done (the w2 items add into the sum only after that); then the first one's
+// they zero the FP32 sum (and, with split w13 items, the partial
+// pre-activation sums) with device-coherent stores and count themselves
+// done (the items add into those sums only after that); then the first one's
 // first wave sorts the pairs into the workspace (results the host may read;
 // the GEMM items look their tiles up from the ids).  With no tile at all no
 // GEMM item runs: the last prep workgroup writes the zero output and clears
 // the counter itself.
 __device__ void decode_prep(const GemmArgs &a13, const GemmArgs &a2, const Workspace &ws, int T,
-                            int H, int wg)
+                            int H, int max_tiles, int wg)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last, s_ntiles;
@@ -1957,6 +2026,12 @@ __device__ void decode_prep(const GemmArgs &a13, const GemmArgs &a2, const Works
     uint64_t *o = reinterpret_cast<uint64_t *>(ws.out_f32);
     for (int i = gid; i < T * H / 2; i += nthr)
         __hip_atomic_store(o + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a13.ksplit > 1) {
+        uint64_t *h = reinterpret_cast<uint64_t *>(a13.hsum);
+        const int nh = max_tiles * kDecodeRows * a13.N;   // 2N floats per tile row
+        for (int i = gid; i < nh; i += nthr)
+            __hip_atomic_store(h + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's stores are performed
     __syncthreads();
     if (tid == 0)
@@ -1988,19 +2063,21 @@ __device__ void decode_prep(const GemmArgs &a13, const GemmArgs &a2, const Works
 }
 
 // The whole decode-shaped layer in one launch: workgroups [0, n_pre) are the
-// prep (decode_prep), then the w13 (tile, column block) items, tile-major,
-// then the w2 items.  Workgroups are dispatched in id order, so every item a
+// prep (decode_prep), then the w13 (tile, column block, K slice) items,
+// tile-major, then the w2 items.  Workgroups are dispatched in id order, so every item a
 // workgroup waits for has been dispatched before it.
 template <int BITS, int GS, int D13, int D2, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_layer_kernel(
     const GemmArgs a13, const GemmArgs a2, const Workspace ws, int T, int H, int max_tiles,
     int nblk13, int nblk2)
 {
-    const int id = (int)blockIdx.x - a13.n_pre, n13 = max_tiles * nblk13;
+    const int per13 = nblk13 * a13.ksplit;   // w13 items per tile
+    const int id = (int)blockIdx.x - a13.n_pre, n13 = max_tiles * per13;
     if (id < 0)
-        decode_prep(a13, a2, ws, T, H, (int)blockIdx.x);
+        decode_prep(a13, a2, ws, T, H, max_tiles, (int)blockIdx.x);
     else if (id < n13)
-        Stream<BITS, GS, 2, D13, true, true, PREP, true>::run(a13, id / nblk13, id % nblk13);
+        Stream<BITS, GS, 2, D13, true, true, PREP, true>::run(
+            a13, id / per13, (id % per13) / a13.ksplit, (id % per13) % a13.ksplit);
     else
         Stream<BITS, GS, 2, D2, false, true, PREP, true>::run(a2, (id - n13) / nblk2,
                                                               (id - n13) % nblk2);
@@ -2301,6 +2378,7 @@ static GemmArgs w13_args(const int32_t *w13, const uint16_t *s13, const LayerDim
     a.tile_done = ws.tile_done;
     a.prepared = d.prepared;
     a.xcd_first = ws.xcd_first;
+    a.ksplit = 1;
     return a;
 }
 
@@ -2345,11 +2423,25 @@ hipError_t launch_w2(const int32_t *w2, const uint16_t *s2, const float *topk_w,
                               d.variant2, d.max_tiles, stream, ev);
 }
 
+// The shared decode launches' w2 prefetch depth: the stand-alone w2's, or
+// half of it when I holds too few load units (0: neither divides them).
 template <int BITS, int GS>
-static hipError_t decode_dispatch(const GemmArgs &a13, GemmArgs a2, int max_tiles,
-                                  hipStream_t stream, const KernelEvents &ev)
+static int decode_depth2(int I)
 {
-    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
+    constexpr int D2 = stream_depth<BITS, GS, false>();
+    const int nunits = I / Stream<BITS, GS, 2, 1, false>::UK;
+    if (nunits % D2 == 0)
+        return D2;
+    if (D2 > 1 && nunits % (D2 / 2) == 0)
+        return D2 / 2;
+    return 0;
+}
+
+template <int BITS, int GS, int D2>
+static hipError_t decode_dispatch_d(const GemmArgs &a13, GemmArgs a2, int max_tiles,
+                                    hipStream_t stream, const KernelEvents &ev)
+{
+    constexpr int D13 = stream_depth<BITS, GS, true>();
     using S13 = Stream<BITS, GS, 2, D13, true, true>;
     using S2 = Stream<BITS, GS, 2, D2, false, true>;
     const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
@@ -2369,12 +2461,25 @@ static hipError_t decode_dispatch(const GemmArgs &a13, GemmArgs a2, int max_tile
 }
 
 template <int BITS, int GS>
+static hipError_t decode_dispatch(const GemmArgs &a13, const GemmArgs &a2, int max_tiles,
+                                  hipStream_t stream, const KernelEvents &ev)
+{
+    constexpr int D2 = stream_depth<BITS, GS, false>();
+    const int d2 = decode_depth2<BITS, GS>(a2.K);
+    if (d2 == D2)
+        return decode_dispatch_d<BITS, GS, D2>(a13, a2, max_tiles, stream, ev);
+    if constexpr (D2 > 1)
+        if (d2 == D2 / 2)
+            return decode_dispatch_d<BITS, GS, D2 / 2>(a13, a2, max_tiles, stream, ev);
+    return hipErrorNotSupported;
+}
+
+template <int BITS, int GS>
 static bool decode_fits(int H, int I)
 {
-    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
-    using S13 = Stream<BITS, GS, 2, D13, true, true>;
-    using S2 = Stream<BITS, GS, 2, D2, false, true>;
-    return (H / S13::UK) % D13 == 0 && (I / S2::UK) % D2 == 0;
+    constexpr int D13 = stream_depth<BITS, GS, true>();
+    return (H / Stream<BITS, GS, 2, D13, true, true>::UK) % D13 == 0 &&
+           decode_depth2<BITS, GS>(I) != 0;
 }
 
 bool decode_one_launch(int bits13, int g13, int bits2, int g2, int H, int I)
@@ -2411,17 +2516,40 @@ hipError_t launch_decode(const int32_t *w13, const uint16_t *s13, const int32_t 
     }
 }
 
+// K slices per w13 (tile, column block) in the single launch: split (2 or 4)
+// while the w13 items would fill fewer than 3 workgroups per CU and every
+// slice keeps whole rounds of the prefetch depth.
+constexpr int kSplitMaxItems = 768;
 template <int BITS, int GS>
-static hipError_t decode_layer_dispatch(const uint16_t *x, const int32_t *ids, GemmArgs a13,
-                                        GemmArgs a2, const LayerDims &d, const Workspace &ws,
-                                        hipStream_t stream, const KernelEvents &ev)
+static int decode_ksplit(int H, int max_tiles, int nblk13)
 {
-    constexpr int D13 = stream_depth<BITS, GS, true>(), D2 = stream_depth<BITS, GS, false>();
+    constexpr int D13 = stream_depth<BITS, GS, true>();
+    const int nunits = H / Stream<BITS, GS, 2, D13, true, true>::UK;
+    int S = 1;
+    while (S < 4 && (long)max_tiles * nblk13 * (2 * S) <= kSplitMaxItems &&
+           nunits % (2 * S * D13) == 0 && max_tiles * nblk13 <= kSyncSplits)
+        S *= 2;
+    return S;
+}
+
+template <int BITS, int GS, int D2>
+static hipError_t decode_layer_dispatch_d(const uint16_t *x, const int32_t *ids, GemmArgs a13,
+                                          GemmArgs a2, const LayerDims &d, const Workspace &ws,
+                                          hipStream_t stream, const KernelEvents &ev)
+{
+    constexpr int D13 = stream_depth<BITS, GS, true>();
     using S13 = Stream<BITS, GS, 2, D13, true, true, false, true>;
     using S2 = Stream<BITS, GS, 2, D2, false, true, false, true>;
     const int nblk13 = a13.N / S13::BN, nblk2 = a2.N / S2::BN;
-    const long prep_threads = (long)d.T * d.H / 8;   // 4 zeroing stores each
-    const int n_pre = (int)((prep_threads + 255) / 256);
+    const int ksplit = ws.hsum ? decode_ksplit<BITS, GS>(d.H, d.max_tiles, nblk13) : 1;
+    if (ksplit != decode_layer_ksplit(BITS, GS, d.H, d.I, d.max_tiles))
+        return hipErrorInvalidValue;   // the plan reports the same split
+    // zeroing: 4 stores of the FP32 sum per thread, and at most 8 of the
+    // split sums
+    const long prep_threads = (long)d.T * d.H / 8;
+    const long hsum_threads = ksplit > 1 ? ((long)d.max_tiles * kDecodeRows * d.I + 7) / 8 : 0;
+    const long nthr = prep_threads > hsum_threads ? prep_threads : hsum_threads;
+    const int n_pre = (int)((nthr + 255) / 256);
     if (d.T * d.topk > kSingleLaunchPairs || d.max_tiles > kSyncTiles || nblk2 > kSyncBlocks ||
         d.block_m != kDecodeRows || n_pre < 1)
         return hipErrorInvalidValue;
@@ -2433,18 +2561,22 @@ static hipError_t decode_layer_dispatch(const uint16_t *x, const int32_t *ids, G
         a->blocks_done = ws.blocks_done;
         a->tile_done = ws.sync_tiles;
         a->status = ws.meta + 2;
+        a->ksplit = 1;
     }
     a13.a = x;   // staged straight from the input rows
+    a13.ksplit = ksplit;
+    a13.hsum = ws.hsum;
+    a13.split_done = ws.sync_split;
     a13.nblk_self = nblk13;
     a2.nblk_self = nblk2;
     a2.tile_target = nblk13;
     a2.done = ws.sync_done;
-    size_t lds = S13::lds_bytes(a13.K);
+    size_t lds = S13::lds_bytes(a13.K / ksplit);
     if (S2::lds_bytes(a2.K) > lds)
         lds = S2::lds_bytes(a2.K);
     if ((size_t)2 * d.E * sizeof(int) > lds)   // the sort's per-expert counts and offsets
         lds = (size_t)2 * d.E * sizeof(int);
-    const dim3 grid((unsigned)(n_pre + d.max_tiles * (nblk13 + nblk2)));
+    const dim3 grid((unsigned)(n_pre + d.max_tiles * (nblk13 * ksplit + nblk2)));
     if (a13.prepared)
         hipExtLaunchKernelGGL((decode_layer_kernel<BITS, GS, D13, D2, true>), grid, dim3(256),
                               (uint32_t)lds, stream, ev.start, ev.stop, 0, a13, a2, ws, d.T,
@@ -2454,6 +2586,35 @@ static hipError_t decode_layer_dispatch(const uint16_t *x, const int32_t *ids, G
                               (uint32_t)lds, stream, ev.start, ev.stop, 0, a13, a2, ws, d.T,
                               d.H, d.max_tiles, nblk13, nblk2);
     return hipGetLastError();
+}
+
+template <int BITS, int GS>
+static hipError_t decode_layer_dispatch(const uint16_t *x, const int32_t *ids,
+                                        const GemmArgs &a13, const GemmArgs &a2,
+                                        const LayerDims &d, const Workspace &ws,
+                                        hipStream_t stream, const KernelEvents &ev)
+{
+    constexpr int D2 = stream_depth<BITS, GS, false>();
+    const int d2 = decode_depth2<BITS, GS>(a2.K);
+    if (d2 == D2)
+        return decode_layer_dispatch_d<BITS, GS, D2>(x, ids, a13, a2, d, ws, stream, ev);
+    if constexpr (D2 > 1)
+        if (d2 == D2 / 2)
+            return decode_layer_dispatch_d<BITS, GS, D2 / 2>(x, ids, a13, a2, d, ws, stream, ev);
+    return hipErrorNotSupported;
+}
+
+int decode_layer_ksplit(int bits, int gs, int H, int I, int max_tiles)
+{
+    const int nblk13 = I / 64;   // w13 items cover 64 act columns
+    switch (bits * 1000 + gs) {
+    case 2064: return decode_ksplit<2, 64>(H, max_tiles, nblk13);
+    case 2128: return decode_ksplit<2, 128>(H, max_tiles, nblk13);
+    case 4032: return decode_ksplit<4, 32>(H, max_tiles, nblk13);
+    case 4064: return decode_ksplit<4, 64>(H, max_tiles, nblk13);
+    case 4128: return decode_ksplit<4, 128>(H, max_tiles, nblk13);
+    default: return 1;
+    }
 }
 
 hipError_t launch_decode_layer(const uint16_t *x, const int32_t *topk_ids, const int32_t *w13,

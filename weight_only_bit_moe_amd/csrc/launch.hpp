@@ -30,6 +30,8 @@ struct Workspace {
     int32_t *blocks_done;     // down-projection column blocks finished
     int32_t *sync_tiles;      // [kSyncTiles][16]: gate/up workgroups finished per tile
     int32_t *sync_done;       // [kSyncBlocks][16]: down workgroups finished per column block
+    int32_t *sync_split;      // [kSyncSplits]: split w13 slices finished per (tile, column block)
+    float *hsum;              // [tile rows][2I] split w13 partial sums (null: no room, no split)
 };
 
 // Fixed region at the start of every workspace (byte offsets): the status
@@ -38,7 +40,9 @@ constexpr size_t kSyncBytes = 32768;
 constexpr size_t kSyncPrepDone = 256, kSyncBlocksDone = 320, kSyncTilesAt = 1024;
 constexpr int kSyncTiles = 128, kSyncBlocks = 128;
 constexpr size_t kSyncDoneAt = kSyncTilesAt + (size_t)kSyncTiles * 64;
-static_assert(kSyncDoneAt + (size_t)kSyncBlocks * 64 <= kSyncBytes, "sync region");
+constexpr size_t kSyncSplitAt = kSyncDoneAt + (size_t)kSyncBlocks * 64;
+constexpr int kSyncSplits = 2048;
+static_assert(kSyncSplitAt + (size_t)kSyncSplits * 4 <= kSyncBytes, "sync region");
 
 // Entries per GEMM of the tile kernel's XCD split: 8 range starts and the total.
 constexpr int kSplitEntries = 9;
@@ -112,6 +116,8 @@ hipError_t launch_decode_layer(const uint16_t *x, const int32_t *topk_ids, const
                                hipStream_t stream, const KernelEvents &ev, uint16_t *out_bf16);
 // Pairs up to which the single-launch decode's tile lookup works (one wave).
 constexpr int kSingleLaunchPairs = 64;
+// K slices per w13 (tile, column block) in the single launch (1, 2 or 4).
+int decode_layer_ksplit(int bits, int gs, int H, int I, int max_tiles);
 // Largest T*H whose BF16 rounding the decode w2 kernel does itself (the last
 // workgroup of each column block rounds that block).
 constexpr size_t kFusedConvertMax = 1 << 18;
