@@ -80,6 +80,66 @@ def assert_sync_clear(workspace, sp):
     assert not sync.any(), f"sync counters left non-zero at bytes {np.flatnonzero(sync)[:8]}"
 
 
+def xcd_split_model(sorted_ids, ntiles, P, nblk, cap):
+    """Host model of the tile kernels' XCD split (the range starts the split
+    launch leaves in workspace ints 8..25 for one GEMM): each tile costs 3 +
+    its active 16-row slices; range x (1..7) starts at the first item whose
+    preceding cost reaches x/8 of the total, inside its tile in proportion to
+    the cost; the starts are kept in order, then every range is capped at
+    `cap` items, forward and back."""
+    cost = [3 + sum(1 for s in range(4) if sorted_ids[b * 64 + 16 * s] < P)
+            for b in range(ntiles)]
+    C = sum(cost)
+    B = [0] * 9
+    B[8] = ntiles * nblk
+    S = 0
+    for b, c in enumerate(cost):
+        for x in range(1, 8):
+            t = x * C
+            if 8 * S < t <= 8 * (S + c):
+                num, den = t - 8 * S, 8 * c
+                B[x] = b * nblk + (nblk * num + den - 1) // den
+        S += c
+    for x in range(1, 8):
+        B[x] = max(B[x - 1], min(B[x], B[8]))
+    for x in range(1, 8):
+        B[x] = min(B[x], B[x - 1] + cap)
+    for x in range(7, 0, -1):
+        B[x] = max(B[x], B[x + 1] - cap)
+    return B
+
+
+def xcd_split_caps(plan, H, I):
+    """(nblk, cap) of the w13 and w2 tile launches: 256 gate/up output
+    columns and 512 down output columns per workgroup; slots per XCD = 1.5 x
+    the even share of max_tiles items plus one tile's items."""
+    out = []
+    for n, outc in ((I, 256), (H, 512)):
+        nblk = -(-n // outc)
+        per = -(-plan["max_tiles"] * nblk // 8)
+        out.append((nblk, per + per // 2 + nblk))
+    return out
+
+
+def assert_xcd_split(L, workspace):
+    """The split the layer ran (workspace ints 8..25) equals the host model."""
+    sp = L.spec
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                            (sp.bits2, sp.group2))
+    assert plan["block_m"] == 64
+    srt = M.workspace_sort(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk, 64)
+    ntiles = int(srt["num_tiles"])
+    sorted_ids = srt["sorted_ids"]
+    table = workspace_meta(workspace, sp)[8:26].reshape(2, 9)
+    for got, (nblk, cap) in zip(table, xcd_split_caps(plan, sp.H, sp.I)):
+        want = xcd_split_model(sorted_ids, ntiles, sp.T * sp.topk, nblk, cap)
+        assert list(got) == want, (list(got), want)
+
+
+def workspace_meta(workspace, sp):
+    return M.workspace_meta(workspace, sp.T, sp.H, sp.I, sp.E, sp.topk).cpu().numpy()
+
+
 def layer_sort(L, workspace):
     """The expert sort a completed forward on layer L ran (plan's block_m)."""
     sp = L.spec

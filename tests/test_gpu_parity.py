@@ -498,6 +498,8 @@ def test_full_workload_sampled_tokens(dev, cfg):
     assert len(rows) == min(sp.T, 64)
     ref = O.forward_layer(L, tokens=rows)
     G.assert_parity(y[rows], ref, f"config {cfg}")
+    if cfg in (4, 5):   # 372 and 1139 tiles: the split's chunk carry (above 1024)
+        G.assert_xcd_split(L, ws)
 
 
 @pytest.mark.parametrize("shard", ["ep8", "tp4"])
@@ -552,6 +554,26 @@ def test_layer_sort_bit_exact_across_sort_paths(dev, T, k, routing, bad):
     G.assert_parity(got, O.forward_layer(L), f"P={P}")
 
 
+def test_tile_split_beyond_4096_tiles(dev):
+    """5120 tiles of 64 rows (1024 experts with 257 pairs each): the XCD split
+    recomputes the costs of tiles past its register cache (4096 tiles) and
+    carries its scan over five 1024-tile chunks.  Its ranges must equal the
+    host model, and every token's output the oracle's."""
+    E, k = 1024, 8
+    T = 257 * E // k
+    sp = spec(T=T, H=128, I=128, E=E, topk=k, **ACT)
+    L = make_layer(sp, seed=33)
+    L.topk_ids = (np.arange(T * k, dtype=np.int64).reshape(T, k) % E).astype(np.int32)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (sp.bits13, sp.group13),
+                            (sp.bits2, sp.group2))
+    assert plan["w13_variant"] == PRE and plan["block_m"] == 64
+    ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
+    _, got = G.run_layer(L, dev, workspace=ws)
+    assert int(G.workspace_meta(ws, sp)[0]) == 5 * E
+    G.assert_xcd_split(L, ws)
+    G.assert_parity(got, O.forward_layer(L), "5120 tiles")
+
+
 def test_tile_split_ranges_capped_at_launch_slots(dev):
     """Prefill-shaped plan whose cost-balanced XCD split needs the cap: 108
     full 64-row tiles of expert 0 followed by 27 one-row experts.  With one
@@ -573,6 +595,7 @@ def test_tile_split_ranges_capped_at_launch_slots(dev):
     ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
     _, got = G.run_layer(L, dev, workspace=ws)
     G.assert_parity(got, O.forward_layer(L), "capped XCD split")
+    G.assert_xcd_split(L, ws)
     table = ws[:128].view(torch.int32)[8:26].cpu().numpy().reshape(2, 9)
     ntiles = nfull + nsmall
     max_tiles = plan["max_tiles"]

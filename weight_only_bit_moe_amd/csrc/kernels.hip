@@ -2263,6 +2263,8 @@ __global__ __launch_bounds__(1024) void split_kernel(const int32_t *__restrict__
         for (int x = 1; x < 8; ++x)   // the tile's items up to the cost target
             B[x] = ntiles == 0 ? 0
                                : rec_b[x] * nblk + (nblk * rec_num[x] + rec_den[x] - 1) / rec_den[x];
+        for (int x = 1; x < 8; ++x)   // ranges in order and inside the item count
+            B[x] = max(B[x - 1], min(B[x], B[8]));
         for (int x = 1; x < 8; ++x)
             B[x] = min(B[x], B[x - 1] + cap);
         for (int x = 7; x >= 1; --x)
