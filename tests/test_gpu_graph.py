@@ -30,8 +30,13 @@ def spec(**kw):
 
 
 CASES = {
-    # one shared decode launch with the BF16 rounding inside it
+    # 16 pairs: the whole layer as one launch
     "decode_shared_launch": (spec(), False),
+    # the single launch with gate/up items split over 4 K slices
+    "decode_single_split": (spec(H=4096, E=64, topk=6), False),
+    # 80 pairs: the routing launch, then one shared w13 + w2 launch with the
+    # BF16 rounding inside it
+    "decode_shared_80_pairs": (spec(T=20, E=32), False),
     "decode_prepared": (spec(), True),
     # separate decode launches (different formats)
     "decode_two_formats": (spec(T=6, bits2=4, group2=64), False),

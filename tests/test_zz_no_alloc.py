@@ -21,7 +21,7 @@ import torch
 import weight_only_bit_moe_amd as M
 from oracle import oracle as O
 from tests import _gpu as G
-from weight_only_bit_moe_amd.inputs import CONFIGS, LayerSpec, make_config, make_layer
+from weight_only_bit_moe_amd.inputs import CONFIGS, LayerSpec, make_config, make_layer, shard_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -80,8 +80,11 @@ def check_pair(L, dev):
 
 
 CASES = {
-    # the decode workload at full size (one shared w13 + w2 launch), then 2 tokens
+    # the decode workload at full size (the whole layer in one launch), then 2 tokens
     "decode_w2g128_full": (lambda: make_config(2), 2),
+    # one GPU's share under tensor parallelism 4 (I = 512): the single launch
+    # with gate/up items split over K slices and their partial-sum buffer
+    "decode_tp4_share": (lambda: make_layer(shard_spec(2, "tp4"), 2), 2),
     # top-1: bit-exact against forward; decode-shaped, separate launches
     "decode_top1": (lambda: make_layer(spec(T=12, H=512, I=256, E=16, topk=1, bits13=2,
                                             bits2=2), seed=5), 5),
