@@ -338,6 +338,29 @@ def test_reused_workspace_and_output(dev):
     G.assert_parity(y, O.forward_layer(small), "reuse")
 
 
+@pytest.mark.parametrize("case", ["one_token_top64", "one_expert", "two_experts_ragged"])
+def test_single_launch_edge_routings(dev, case):
+    """Single-launch edge cases at the 64-pair limit: one token with top-64
+    over 64 experts (every tile one pair plus padding), 64 pairs on one
+    expert (16 full tiles of one expert), and two experts with 61 + 3 pairs
+    (ragged last tiles)."""
+    if case == "one_token_top64":
+        sp = spec(T=1, H=1024, I=1024, E=64, topk=64, bits13=2, bits2=2, **ACT)
+    else:
+        sp = spec(T=16, H=1024, I=1024, E=16, topk=4, bits13=2, bits2=2, **ACT)
+    plan = M.moe_wna16_plan(sp.T, sp.H, sp.I, sp.E, sp.topk, (2, 128), (2, 128))
+    assert plan["single_launch"] == 1
+    L = make_layer(sp, seed=140)
+    if case == "one_expert":
+        L.topk_ids[:, :] = 5          # duplicates within every token
+    elif case == "two_experts_ragged":
+        ids = np.full(sp.T * sp.topk, 2, np.int32)
+        ids[[7, 30, 63]] = 6
+        L.topk_ids = ids.reshape(sp.T, sp.topk)
+    _, got = G.run_layer(L, dev)
+    G.assert_parity(got, O.forward_layer(L), case)
+
+
 @pytest.mark.parametrize("q", [(2, 64), (2, 128), (4, 32), (4, 64), (4, 128)])
 def test_single_launch_back_to_back_calls(dev, q):
     """The single-launch decode plan (routing, reorder, zeroing, both GEMMs
