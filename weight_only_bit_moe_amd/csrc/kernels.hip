@@ -812,7 +812,7 @@ struct Tile {
     static constexpr int SC_WAVE = GPC * 64 * 4;
     static constexpr int BI_OFF = SC_OFF + NW * SC_WAVE;
     static constexpr int STAGE = BI_OFF + GPC * 64 * 4;
-    static constexpr int kLdsBudget = 160 * 1024 - 1024;   // the rest holds the row table
+    static constexpr int kLdsBudget = 160 * 1024 - 2048;   // the rest holds the row table
     static constexpr int STAGES = kLdsBudget / STAGE >= 4 ? 4 : kLdsBudget / STAGE;
     static_assert(STAGES >= 2, "two chunks must fit in LDS");
     static constexpr int LDS_BYTES = STAGES * STAGE;
@@ -826,7 +826,18 @@ struct Tile {
         int pair[BM];
         int src[BM];
         int real;
+        size_t orow[BM];   // staged w2 epilogue: the output row's offset (token * N)
+        float w[BM];       // staged w2 epilogue: the routing weight
     };
+    // The w2 epilogue stages each wave's 64 x 64 result through LDS when the
+    // ring can hold all eight (rows padded to 68 floats against bank
+    // conflicts): then every atomic instruction adds 64 consecutive floats of
+    // one output row, two full cache lines, instead of 16 floats of each of
+    // 4 rows.  The FP32 atomics are performed per line, so this halves their
+    // count (prefill w2 launches 7-8 % shorter).  Group-32 formats, whose
+    // rings are smaller, keep the direct form.
+    static constexpr int EPI_STRIDE = 68;
+    static constexpr bool STAGED_EPI = LDS_BYTES >= NW * 64 * EPI_STRIDE * 4;
 
     // 16-byte piece position inside a row's chunk of codes: XOR-swizzled so
     // that the 8 (or 16) lanes of one LDS access phase hit distinct banks.
@@ -1192,6 +1203,34 @@ struct Tile {
         const int rows_real = rows.real;
         if constexpr (W13) {
             epilogue_w13<MTA>(reinterpret_cast<EpiW13 *>(lds), args, acc, cx, rows_real);
+        } else if constexpr (STAGED_EPI) {
+            // routing-weighted scatter-add into the FP32 accumulator through
+            // the LDS tile (the ring is free: every wave is past the barrier
+            // above); each row's output offset and weight are computed once
+            Rows &rw = const_cast<Rows &>(rows);
+            if (cx.tid < rows_real) {
+                const int p = rows.pair[cx.tid];
+                rw.orow[cx.tid] = (size_t)(p / args.topk) * args.N;
+                rw.w[cx.tid] = args.topk_w[p];
+            }
+            float *tile = reinterpret_cast<float *>(lds) + cx.wave * 64 * EPI_STRIDE;
+            if (cx.wave_on) {
+                const int g = cx.g, c = cx.lane & 15;
+#pragma unroll
+                for (int i = 0; i < MTA; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            tile[(16 * i + 4 * g + v) * EPI_STRIDE + 16 * j + c] = acc[i][j][v];
+            }
+            __syncthreads();
+            if (!cx.wave_on)
+                return;
+            float *out = args.out_f32 + cx.col0 + cx.lane;   // the wave's 64 columns
+#pragma unroll 4
+            for (int r = 0; r < rows_real; ++r)
+                unsafeAtomicAdd(out + rows.orow[r], rows.w[r] * tile[r * EPI_STRIDE + cx.lane]);
         } else {
             if (!cx.wave_on)
                 return;
