@@ -430,48 +430,6 @@ __device__ __forceinline__ void store_coherent(float *p, float v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// x in MFMA fragment order with minus its per-group bias term, for thread
-// `gid` of T * H / 8: GS / 8 consecutive threads per (token, group), 8
-// fragment positions each (one 16-byte store); the group's bias term is
-// summed across them with shuffles, so the threads of a group must run
-// together (whole groups per wave: GS / 8 divides 64).
-template <int BITS, int GS>
-__device__ __forceinline__ void prep_x(const uint16_t *__restrict__ x, const Workspace &ws, int T,
-                                       int H, int gid)
-{
-    constexpr int PL = GS / 8;
-    const int ngroups = H / GS;
-    const bool on = gid < T * ngroups * PL;
-    const int q = gid % PL, tg = gid / PL;
-    const int t = on ? tg / ngroups : 0, G = on ? tg % ngroups : 0;
-    const uint16_t *src = x + (size_t)t * H + (size_t)G * GS;
-    uint32_t e[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v)
-        e[v] = on ? src[frag_src(BITS, GS, q * 8 + v)] : 0u;
-    float sum = 0.f;  // sum of (stored activation) * (its bias weight)
-    u32x4_t o;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const int p0 = q * 8 + 2 * h, p1 = p0 + 1;
-        const uint32_t lo = bf16_scaled(e[2 * h], frag_shift(BITS, GS, p0));
-        const uint32_t hi = bf16_scaled(e[2 * h + 1], frag_shift(BITS, GS, p1));
-        sum += bf16_to_f32(lo) * (float)frag_bias_weight(BITS, GS, p0);
-        sum += bf16_to_f32(hi) * (float)frag_bias_weight(BITS, GS, p1);
-        o[h] = lo | (hi << 16);
-    }
-#pragma unroll
-    for (int m = 1; m < PL; m <<= 1)
-        sum += __shfl_xor(sum, m, 64);
-    if (on) {
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS) + q;
-        float *bias = ws.x_bias + (size_t)t * ngroups + G;
-        *dst = o;
-        if (q == 0)
-            *bias = -sum;   // stored negated: the chain start
-    }
-}
-
 // The 8 consecutive fragment positions [8q, 8q + 8) of one group, from the
 // raw BF16 words `w` that frag_chunk_load fetched: position 8q + v holds the
 // group element that word half (v >> 1) + 4 (v & 1) carries (see frag_src),
@@ -511,6 +469,36 @@ __device__ __forceinline__ u32x4_t frag_chunk_load(const uint16_t *grp, int q)
         const u32x2_t a = *reinterpret_cast<const u32x2_t *>(grp + base);
         const u32x2_t b = *reinterpret_cast<const u32x2_t *>(grp + base + 8);
         return u32x4_t{a[0], a[1], b[0], b[1]};
+    }
+}
+
+// x in MFMA fragment order with minus its per-group bias term, for thread
+// `gid` of T * H / 8: GS / 8 consecutive threads per (token, group), 8
+// fragment positions each (one 16-byte store); the group's bias term is
+// summed across them with shuffles, so the threads of a group must run
+// together (whole groups per wave: GS / 8 divides 64).
+template <int BITS, int GS>
+__device__ __forceinline__ void prep_x(const uint16_t *__restrict__ x, const Workspace &ws, int T,
+                                       int H, int gid)
+{
+    constexpr int PL = GS / 8;
+    const int ngroups = H / GS;
+    const bool on = gid < T * ngroups * PL;
+    const int q = gid % PL, tg = gid / PL;
+    const int t = on ? tg / ngroups : 0, G = on ? tg % ngroups : 0;
+    const u32x4_t raw = on ? frag_chunk_load<BITS, GS>(x + (size_t)t * H + (size_t)G * GS, q)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+    float sum = 0.f;  // sum of (stored activation) * (its bias weight)
+    const u32x4_t o = frag_chunk<BITS, GS>(raw, q, sum);
+#pragma unroll
+    for (int m = 1; m < PL; m <<= 1)
+        sum += __shfl_xor(sum, m, 64);
+    if (on) {
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(ws.x_perm + (size_t)t * H + (size_t)G * GS) + q;
+        float *bias = ws.x_bias + (size_t)t * ngroups + G;
+        *dst = o;
+        if (q == 0)
+            *bias = -sum;   // stored negated: the chain start
     }
 }
 
@@ -1298,19 +1286,12 @@ struct Tile {
         const int pieces = ncols / 8;
         for (int q = tid; q < rows_real * pieces; q += NTHREADS) {
             const int r = q / pieces, c8 = q % pieces;
-            const int gl = (c8 * 8) / G2, pos0 = (c8 * 8) % G2;
-            const uint16_t *arow = epi->act + r * ACT_STRIDE + gl * G2;
-            u32x4_t o;
+            const int gl = (c8 * 8) / G2, q8 = ((c8 * 8) % G2) / 8;
+            // the group's elements for positions [8 q8, 8 q8 + 8), from the
+            // row's LDS copy (16-byte aligned groups)
+            const u32x4_t raw = frag_chunk_load<B2, G2>(epi->act + r * ACT_STRIDE + gl * G2, q8);
             float sum = 0.f;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int p0 = pos0 + 2 * h, p1 = p0 + 1;
-                const uint32_t lo = bf16_scaled(arow[frag_src(B2, G2, p0)], frag_shift(B2, G2, p0));
-                const uint32_t hi = bf16_scaled(arow[frag_src(B2, G2, p1)], frag_shift(B2, G2, p1));
-                sum += bf16_to_f32(lo) * (float)frag_bias_weight(B2, G2, p0);
-                sum += bf16_to_f32(hi) * (float)frag_bias_weight(B2, G2, p1);
-                o[h] = lo | (hi << 16);
-            }
+            const u32x4_t o = frag_chunk<B2, G2>(raw, q8, sum);
             *reinterpret_cast<u32x4_t *>(args.act_out + (size_t)(cx.b * BM + r) * args.N +
                                          cx.nb * OUTC + c8 * 8) = o;
             epi->part[r * (OUTC / 8) + c8] = sum;
