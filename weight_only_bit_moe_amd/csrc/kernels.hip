@@ -997,10 +997,13 @@ struct Tile {
     {
         const int g = cx.g, c = cx.lane & 15;
         const unsigned char *st = lds + stage * STAGE;
-        auto scales = [&](int G) {
-            return *reinterpret_cast<const u32x4_t *>(
+        // the chunk's scales, read once for all row subtiles
+        u32x4_t sc[GPC];
+#pragma unroll
+        for (int G = 0; G < GPC; ++G)
+            sc[G] = *reinterpret_cast<const u32x4_t *>(
                 st + SC_OFF + ((cx.wave * GPC + G) * 64 + c * 4) * 4);
-        };
+        auto scales = [&](int G) { return sc[G]; };
         f32x4_t pend[NT];   // last chain of the previous subtile, not yet folded
 #pragma unroll
         for (int i = 0; i < MTA; ++i) {
