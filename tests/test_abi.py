@@ -64,6 +64,21 @@ def test_plan_picks_tiles_from_rows_per_expert(lib):
     assert big["w13_variant"] == 1
 
 
+def test_plan_decode_lds_limits(lib):
+    """The decode-shaped kernels hold whole activation rows and the
+    workgroup's scales in at most 64 KB of LDS: hidden (or intermediate)
+    sizes up to 5376 for groups of 128 and 3328 for 2-bit groups of 32 stay
+    decode-shaped, one step more goes to the tile kernel; the single launch
+    (both GEMMs in one launch) stops at 5120."""
+    for q, last in [((2, 128), 5376), ((4, 128), 5376), ((2, 32), 3328), ((4, 64), 4480)]:
+        assert M.moe_wna16_plan(4, last, 256, 8, 2, q, q)["w13_variant"] == 2, q
+        assert M.moe_wna16_plan(4, last + 128, 256, 8, 2, q, q)["w13_variant"] == 1, q
+        assert M.moe_wna16_plan(4, 1024, last, 8, 2, q, q)["w2_variant"] == 2, q
+        assert M.moe_wna16_plan(4, 1024, last + 128, 8, 2, q, q)["w2_variant"] == 1, q
+    assert M.moe_wna16_plan(4, 5120, 512, 8, 2, (4, 128), (4, 128))["single_launch"] == 1
+    assert M.moe_wna16_plan(4, 5248, 512, 8, 2, (4, 128), (4, 128))["single_launch"] == 0
+
+
 def test_plan_reports_shared_launches(lib):
     dec = M.moe_wna16_plan(4, 4096, 2048, 256, 6, (2, 128), (2, 128))
     assert dec["gemms_one_launch"] == 1 and dec["convert_in_w2"] == 1

@@ -172,6 +172,19 @@ SMALL = {
                         None, PRE),
     "pre_max_topk": (spec(T=40, H=256, I=128, E=64, topk=64, group13=64, group2=32),
                      None, PRE),
+    # the largest sizes the decode-shaped kernels take (their LDS image at
+    # the 64 KB limit: 5376 for groups of 128, 3328 for 2-bit groups of 32),
+    # one step past it (the tile kernel), the largest single-launch hidden
+    # size, and a long K for the tile kernel (128 chunks, 32 w2 column blocks)
+    "dec_lds_limit_h5376": (spec(T=4, H=5376, I=256, E=8, topk=2, bits13=2, bits2=2, **ACT),
+                            None, DEC),
+    "pre_past_lds_limit_h5504": (spec(T=4, H=5504, I=256, E=8, topk=2, bits13=2, bits2=2),
+                                 None, PRE),
+    "dec_lds_limit_i5376": (spec(T=4, H=256, I=5376, E=8, topk=2, **ACT), None, DEC),
+    "dec_lds_limit_g32_h3328": (spec(T=4, H=3328, I=256, E=8, topk=2, bits13=2, group13=32,
+                                     bits2=2, group2=32), None, DEC),
+    "dec_single_launch_h5120": (spec(T=4, H=5120, I=512, E=8, topk=2, **ACT), None, DEC),
+    "pre_h16384": (spec(T=6, H=16384, I=256, E=4, topk=2, **ACT), None, PRE),
     # H = 640: the last w2 column block is partly idle (640 = 512 + 128)
     "pre_w2_partial_column_block": (spec(T=64, H=640, I=384, E=3, topk=2, bits13=2,
                                          group13=64, bits2=4, group2=128), None, PRE),
