@@ -603,24 +603,6 @@ struct CodeTraits {
     }
 };
 
-template <int NDW>
-__device__ __forceinline__ void load_codes(uint32_t (&dst)[NDW], const uint32_t *p)
-{
-    if constexpr (NDW == 4) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
-        dst[0] = v[0];
-        dst[1] = v[1];
-        dst[2] = v[2];
-        dst[3] = v[3];
-    } else if constexpr (NDW == 2) {
-        const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
-        dst[0] = v[0];
-        dst[1] = v[1];
-    } else {
-        dst[0] = *p;
-    }
-}
-
 // Constants of the code unpack held in registers the compiler cannot fold
 // (produced once by a volatile move), so that (x & mask) | magic is selected
 // as one v_and_or_b32: a VOP3 instruction cannot encode two literals.  The
@@ -1157,7 +1139,7 @@ struct Tile {
     // barrier each wave waits for its copies of chunk k + 1; the copies
     // issued after those are always STAGES - 2 chunks' worth.
     template <int MTA>
-    static __device__ void body(unsigned char *lds, const Rows &rows, const GemmArgs &args,
+    static __device__ void body(unsigned char *lds, Rows &rows, const GemmArgs &args,
                                 const Ctx &cx)
     {
         f32x4_t acc[MTA][NT];
@@ -1198,11 +1180,10 @@ struct Tile {
             // routing-weighted scatter-add into the FP32 accumulator through
             // the LDS tile (the ring is free: every wave is past the barrier
             // above); each row's output offset and weight are computed once
-            Rows &rw = const_cast<Rows &>(rows);
             if (cx.tid < rows_real) {
                 const int p = rows.pair[cx.tid];
-                rw.orow[cx.tid] = (size_t)(p / args.topk) * args.N;
-                rw.w[cx.tid] = args.topk_w[p];
+                rows.orow[cx.tid] = (size_t)(p / args.topk) * args.N;
+                rows.w[cx.tid] = args.topk_w[p];
             }
             float *tile = reinterpret_cast<float *>(lds) + cx.wave * 64 * EPI_STRIDE;
             if (cx.wave_on) {
