@@ -178,3 +178,45 @@ def assert_parity(got, ref, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert r <= 1.0, f"{what}: max error is {r:.3f}x the tolerance"
     return r
+
+
+def sampled_tokens(L, ws, n=64):
+    """Tokens of a full-size prefill-shaped layer worth checking one by one:
+    those in the tiles on both sides of every XCD range boundary of both
+    GEMMs (read from the split table the layer left in its workspace), the
+    first and last tile, tokens routed to the 8 least-used experts, then
+    evenly spaced tokens up to n."""
+    sp = L.spec
+    T, k = sp.T, sp.topk
+    bm, srt = layer_sort(L, ws)
+    meta = M.workspace_meta(ws, T, sp.H, sp.I, sp.E, k).cpu().numpy()
+    ntiles = srt["num_tiles"]
+    picked = []
+
+    def add_tile(b):
+        if 0 <= b < ntiles:
+            rows = srt["sorted_ids"][b * bm:(b + 1) * bm]
+            real = rows[rows < T * k]
+            picked.extend([int(real[0]) // k, int(real[-1]) // k])
+
+    if bm == 64:
+        for g, outc, N in ((0, 256, sp.I), (1, 512, sp.H)):   # items per tile: column blocks
+            nblk = -(-N // outc)
+            first = meta[8 + 9 * g: 17 + 9 * g]
+            for x in range(1, 8):
+                add_tile(int(first[x]) // nblk)
+                add_tile((int(first[x]) - 1) // nblk)
+    add_tile(0)
+    add_tile(ntiles - 1)
+    ids = L.topk_ids
+    counts = np.bincount(ids[(ids >= 0) & (ids < sp.E)].ravel(), minlength=sp.E)
+    for e in np.argsort(np.where(counts > 0, counts, 1 << 30), kind="stable")[:8]:
+        if counts[e]:
+            picked.append(int(np.argwhere(ids == e)[0][0]))
+    out = list(dict.fromkeys(picked))[:n]
+    for t in np.linspace(0, T - 1, n).astype(int):
+        if len(out) >= n:
+            break
+        if t not in out:
+            out.append(int(t))
+    return sorted(out)

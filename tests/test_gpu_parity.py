@@ -475,48 +475,6 @@ def test_shared_launch_small_intermediate(dev, q):
 # full-size workloads, sampled tokens
 # --------------------------------------------------------------------------
 
-def sampled_tokens(L, ws, n=64):
-    """Tokens of a full-size prefill-shaped layer worth checking one by one:
-    those in the tiles on both sides of every XCD range boundary of both
-    GEMMs (read from the split table the layer left in its workspace), the
-    first and last tile, tokens routed to the 8 least-used experts, then
-    evenly spaced tokens up to n."""
-    sp = L.spec
-    T, k = sp.T, sp.topk
-    bm, srt = G.layer_sort(L, ws)
-    meta = M.workspace_meta(ws, T, sp.H, sp.I, sp.E, k).cpu().numpy()
-    ntiles = srt["num_tiles"]
-    picked = []
-
-    def add_tile(b):
-        if 0 <= b < ntiles:
-            rows = srt["sorted_ids"][b * bm:(b + 1) * bm]
-            real = rows[rows < T * k]
-            picked.extend([int(real[0]) // k, int(real[-1]) // k])
-
-    if bm == 64:
-        for g, outc, N in ((0, 256, sp.I), (1, 512, sp.H)):   # items per tile: column blocks
-            nblk = -(-N // outc)
-            first = meta[8 + 9 * g: 17 + 9 * g]
-            for x in range(1, 8):
-                add_tile(int(first[x]) // nblk)
-                add_tile((int(first[x]) - 1) // nblk)
-    add_tile(0)
-    add_tile(ntiles - 1)
-    ids = L.topk_ids
-    counts = np.bincount(ids[(ids >= 0) & (ids < sp.E)].ravel(), minlength=sp.E)
-    for e in np.argsort(np.where(counts > 0, counts, 1 << 30), kind="stable")[:8]:
-        if counts[e]:
-            picked.append(int(np.argwhere(ids == e)[0][0]))
-    out = list(dict.fromkeys(picked))[:n]
-    for t in np.linspace(0, T - 1, n).astype(int):
-        if len(out) >= n:
-            break
-        if t not in out:
-            out.append(int(t))
-    return sorted(out)
-
-
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_workload_sampled_tokens(dev, cfg):
     """The workloads at full size, in the launch configuration bench.py times:
@@ -530,7 +488,7 @@ def test_full_workload_sampled_tokens(dev, cfg):
     ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
     _, y = G.run_layer(L, dev, workspace=ws)
     assert np.all(np.isfinite(y))
-    rows = list(range(sp.T)) if sp.T <= 64 else sampled_tokens(L, ws)
+    rows = list(range(sp.T)) if sp.T <= 64 else G.sampled_tokens(L, ws)
     assert len(rows) == min(sp.T, 64)
     ref = O.forward_layer(L, tokens=rows)
     G.assert_parity(y[rows], ref, f"config {cfg}")
@@ -552,7 +510,7 @@ def test_one_gpu_share_of_sharded_layer(dev, cfg, shard):
     print(f"{sp.name}: T={sp.T} E={sp.E} I={sp.I} k={sp.topk}", flush=True)
     ws = M.workspace_for(sp.T, sp.H, sp.I, sp.E, sp.topk, dev)
     _, y = G.run_layer(L, dev, workspace=ws)
-    rows = list(range(sp.T)) if sp.T <= 64 else sampled_tokens(L, ws)
+    rows = list(range(sp.T)) if sp.T <= 64 else G.sampled_tokens(L, ws)
     G.assert_parity(y[rows], O.forward_layer(L, tokens=rows), sp.name)
     if shard == "ep8":
         local = (L.topk_ids >= 0) & (L.topk_ids < sp.E)
